@@ -1,0 +1,132 @@
+// BlockMask builder (attention-gym "Concepts" page, "BlockMask Internals" and
+// "Key attributes"; paper review "Flex Attention: A Programming Model for
+// Generating Optimized Attention Kernels", §4.1-4.2).
+//
+// One workgroup per BlockMask row (b', h', query tile).  Each wave classifies
+// whole 128x128 tiles: its 64 lanes each own up to two key columns of the
+// tile and walk the tile's in-range query rows, evaluating the mask_mod per
+// position; a wave vote gives "any position attends" / "every position
+// attends".  A tile is empty when none attends, full when all do, partial
+// otherwise.  Wave 0 then appends the tile ids of each class, in ascending
+// order, with a ballot + popcount prefix, so every list is written in order
+// without atomics.  All integer work: the result is bit-exact by construction.
+#include "mods.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kTile = FA_BLOCK;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 256;  // tiles classified per pass (kChunk / kWaves per wave)
+
+enum : int { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+template <class Mask>
+__device__ __forceinline__ int classify_tile(const BuildParams& p, int b, int h, int q0, int qn,
+                                             int kb, int lane) {
+  const int k0 = kb * kTile;
+  const int kn = min(kTile, p.Skv - k0);
+  const bool c0 = lane < kn;
+  const bool c1 = lane + 64 < kn;
+  bool any = false, all = true;
+  for (int i = 0; i < qn; ++i) {
+    const auto r = Mask::row(p.mask, b, h, q0 + i);
+    if (c0) {
+      const bool m = r(k0 + lane);
+      any |= m;
+      all &= m;
+    }
+    if (c1) {
+      const bool m = r(k0 + 64 + lane);
+      any |= m;
+      all &= m;
+    }
+    // Once the wave has seen both an attended and a masked position the
+    // tile is partial whatever the remaining rows hold.
+    if ((i & 7) == 7 && __any(any) && !__all(all)) return kPartial;
+  }
+  if (!__any(any)) return kEmpty;
+  return __all(all) ? kFull : kPartial;
+}
+
+template <class Mask>
+__global__ __launch_bounds__(kThreads) void build_block_mask_kernel(BuildParams p) {
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q0 = qb * kTile;
+  const int qn = min(kTile, p.Sq - q0);
+  const long long row = ((long long)b * p.Hm + h) * p.NQ + qb;
+  int* kv_idx = p.kv_idx + row * p.NK;
+  int* full_idx = p.full_idx + row * p.NK;
+
+  __shared__ unsigned char cls[kChunk];
+  __shared__ int counts[2];
+  if (threadIdx.x == 0) {
+    counts[0] = 0;
+    counts[1] = 0;
+  }
+
+  for (int c0 = 0; c0 < p.NK; c0 += kChunk) {
+    for (int i = 0; i < kChunk / kWaves; ++i) {
+      const int j = i * kWaves + wave;
+      const int kb = c0 + j;
+      if (kb < p.NK) {
+        const int c = classify_tile<Mask>(p, b, h, q0, qn, kb, lane);
+        if (lane == 0) cls[j] = (unsigned char)c;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int np = counts[0], nf = counts[1];
+      const unsigned long long below = (1ull << lane) - 1ull;
+      for (int s = 0; s < kChunk; s += 64) {
+        const int kb = c0 + s + lane;
+        const int c = kb < p.NK ? (int)cls[s + lane] : kEmpty;
+        const bool in_kv = p.separate_full ? (c == kPartial) : (c != kEmpty);
+        const bool in_full = c == kFull;
+        const unsigned long long mk = __ballot(in_kv);
+        const unsigned long long mf = __ballot(in_full);
+        if (in_kv) kv_idx[np + __popcll(mk & below)] = kb;
+        if (in_full) full_idx[nf + __popcll(mf & below)] = kb;
+        np += __popcll(mk);
+        nf += __popcll(mf);
+      }
+      if (lane == 0) {
+        counts[0] = np;
+        counts[1] = nf;
+      }
+    }
+    __syncthreads();
+  }
+
+  const int np = counts[0], nf = counts[1];
+  for (int i = threadIdx.x; i < p.NK; i += kThreads) {
+    if (i >= np) kv_idx[i] = 0;
+    if (i >= nf) full_idx[i] = 0;
+  }
+  if (threadIdx.x == 0) {
+    p.kv_num[row] = np;
+    p.full_num[row] = nf;
+  }
+}
+
+struct LaunchBuild {
+  const BuildParams& p;
+  hipStream_t stream;
+  template <class Mask>
+  void operator()() {
+    dim3 grid(p.NQ, p.Hm, p.Bm);
+    hipLaunchKernelGGL(build_block_mask_kernel<Mask>, grid, dim3(kThreads), 0, stream, p);
+  }
+};
+
+}  // namespace
+
+fa_status launch_block_mask(int mask_kind, const BuildParams& p, hipStream_t stream) {
+  LaunchBuild l{p, stream};
+  if (!dispatch_mask(mask_kind, l)) return FA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa

@@ -1,0 +1,335 @@
+// Split-KV decode with a log-sum-exp merge.
+//
+// One query token per sequence against a long KV cache.  Following the
+// "Flex Decoding" part of the talk summary "FlexAttention: A Flexible and
+// Performant Approach to Transformer Attention", the key axis is split into
+// chunks that are processed in parallel and combined by a final reduction;
+// the score_mod still applies.  The chunks are cut from the sequence's
+// BlockMask row (partial tiles first, then full tiles), so empty tiles past a
+// sequence's valid length are never read (Concepts page, "BlockMask
+// Internals").
+//
+// decode_partial: one 256-thread workgroup per (split, KV head, batch row).
+// It reads each K/V row of its chunk exactly once and serves all G query
+// heads of that KV head from it (GQA).  Pass 1 computes the G scores of every
+// key into LDS (16-byte row loads, a dot product per lane over 8 dims and a
+// cross-lane sum), pass 2 takes each head's max and exponentials, pass 3
+// accumulates P.V.  Its output is the chunk's normalised partial output and
+// base-2 LSE in a caller-provided fp32 workspace.
+// decode_merge: LSE = log-sum-exp of the chunk LSEs, O = sum_s e^(LSE_s - LSE) O_s.
+#include "mods.hpp"
+
+namespace fa {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kMaxBps = 8;  // kv tiles per split at most
+constexpr int kMaxRows = kMaxBps * FA_BLOCK;
+
+struct EvalMask {
+  const MaskParams& mp;
+  int b, h, q, kv;
+  bool result;
+  template <class M>
+  __device__ void operator()() {
+    result = M::row(mp, b, h, q)(kv);
+  }
+};
+
+__device__ __forceinline__ void unpack8(const u32x4_t& x, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(x[i] << 16);
+    f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+  }
+}
+
+template <int D, int G, class Score>
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
+  constexpr int LPR = D / 8;          // lanes per K/V row (16 bytes each)
+  constexpr int RPW = 64 / LPR;       // rows per wave per load
+  constexpr int RSTEP = kDecWaves * RPW;
+  const FwdParams& p = P.f;
+  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPR, rr = lane / LPR;
+
+  __shared__ float sc[G][kMaxRows];
+  __shared__ float red[kDecWaves][G];
+  __shared__ float osum[kDecWaves][G][D];
+
+  // block list of this sequence (row q-tile 0 of its BlockMask)
+  const BlockMaskView& bm = p.bm;
+  int n_part, n_full;
+  const int* part_idx = nullptr;
+  const int* full_idx = nullptr;
+  if (bm.dense) {
+    n_part = 0;
+    n_full = bm.NK;
+  } else {
+    const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hkv * G : 0;
+    const long long row = ((long long)mb * bm.Hm + mh) * bm.NQ;
+    n_part = bm.kv_num[row];
+    part_idx = bm.kv_idx + row * bm.NK;
+    if (bm.separate_full) {
+      n_full = bm.full_num[row];
+      full_idx = bm.full_idx + row * bm.NK;
+    } else {
+      n_full = 0;
+    }
+  }
+  const int T = n_part + n_full;
+  const int t0 = split * P.blocks_per_split;
+  const int t1 = min(T, t0 + P.blocks_per_split);
+  const long long ws_row0 = ((long long)b * p.Hq + (long long)hkv * G) * P.splits + split;
+  if (t0 >= t1) {
+    if (tid < G) P.ws_lse[ws_row0 + (long long)tid * P.splits] = -INFINITY;
+    return;
+  }
+  const int n_rows = (t1 - t0) * FA_BLOCK;
+  auto kb_of = [&](int t) -> int {
+    if (t < n_part) return part_idx[t];
+    return bm.dense ? (t - n_part) : full_idx[t - n_part];
+  };
+
+  const uint16_t* Kp = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1];
+  const uint16_t* Vp = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1];
+
+  // query slices (8 dims per lane) of the G heads
+  float qf[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)(hkv * G + g) * p.qs[1];
+    unpack8(*(const u32x4_t*)(Qp + 8 * sub), qf[g]);
+  }
+  typename Score::Row srow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) srow[g] = Score::row(p.score, b, hkv * G + g, 0);
+
+  // ---- pass 1: scores ---------------------------------------------------------
+  constexpr int U = 4;
+  for (int base = 0; base < n_rows; base += RSTEP * U) {
+    u32x4_t kx[U];
+    int kvs[U];
+    bool part[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rl = base + u * RSTEP + wave * RPW + rr;
+      const int t = t0 + rl / FA_BLOCK;
+      const int kv = kb_of(min(t, t1 - 1)) * FA_BLOCK + rl % FA_BLOCK;
+      kvs[u] = kv;
+      part[u] = t < n_part;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (rl < n_rows && kv < p.Skv) x = *(const u32x4_t*)(Kp + (long long)kv * p.ks[2] + 8 * sub);
+      kx[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rl = base + u * RSTEP + wave * RPW + rr;
+      float kf[8];
+      unpack8(kx[u], kf);
+      float dot[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaf(qf[g][j], kf[j], a);
+        dot[g] = a;
+      }
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) dot[g] += __shfl_xor(dot[g], off);
+      }
+      const int kv = kvs[u];
+      bool keep = kv < p.Skv;
+      if (keep && part[u]) {
+        EvalMask em{p.mask, b, hkv * G, 0, kv, false};
+        dispatch_mask(P.mask_kind, em);
+        keep = em.result;
+      }
+      if (rl < n_rows && sub < G) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (g == sub && keep) x = Score::apply1(srow[g], dot[g], kv, 0);
+        }
+        sc[sub][rl] = x;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: per-head max, exponentials, sums --------------------------------
+  float m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = -INFINITY;
+    for (int i = tid; i < n_rows; i += kDecThreads) v = fmaxf(v, sc[g][i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (lane == 0) red[wave][g] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = red[0][g];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) v = fmaxf(v, red[w][g]);
+    m[g] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mu = m[g] == -INFINITY ? 0.0f : m[g];
+    float s = 0.0f;
+    for (int i = tid; i < n_rows; i += kDecThreads) {
+      const float e = __builtin_amdgcn_exp2f(sc[g][i] - mu);
+      sc[g][i] = e;
+      s += e;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) red[wave][g] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) v += red[w][g];
+    l[g] = v;
+  }
+
+  // ---- pass 3: P.V ------------------------------------------------------------
+  float o[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
+  for (int base = 0; base < n_rows; base += RSTEP * U) {
+    u32x4_t vx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rl = base + u * RSTEP + wave * RPW + rr;
+      const int t = t0 + rl / FA_BLOCK;
+      const int kv = kb_of(min(t, t1 - 1)) * FA_BLOCK + rl % FA_BLOCK;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (rl < n_rows && kv < p.Skv) x = *(const u32x4_t*)(Vp + (long long)kv * p.vs[2] + 8 * sub);
+      vx[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rl = base + u * RSTEP + wave * RPW + rr;
+      if (rl < n_rows) {
+        float vf[8];
+        unpack8(vx[u], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pg = sc[g][rl];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pg, vf[j], o[g][j]);
+        }
+      }
+    }
+  }
+  // sum over the row groups of the wave, then over waves
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] += __shfl_xor(o[g][j], off);
+  }
+  if (rr == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) osum[wave][g][8 * sub + j] = o[g][j];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kDecThreads) {
+    const int g = i / D, d = i % D;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) v += osum[w][g][d];
+    const long long wr = ws_row0 + (long long)g * P.splits;
+    P.ws_o[wr * D + d] = l[g] > 0.0f ? v / l[g] : 0.0f;
+    if (d == 0) P.ws_lse[wr] = l[g] > 0.0f ? m[g] + __log2f(l[g]) : -INFINITY;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams P) {
+  const FwdParams& p = P.f;
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const float* lse = P.ws_lse + (long long)bh * P.splits;
+  float m = -INFINITY;
+  for (int s = 0; s < P.splits; ++s) m = fmaxf(m, lse[s]);
+  float acc = 0.0f, tot = 0.0f;
+  if (m > -INFINITY) {
+    for (int s = 0; s < P.splits; ++s) {
+      const float ls = lse[s];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ls - m);
+      tot += w;
+      acc = fmaf(w, P.ws_o[((long long)bh * P.splits + s) * D + d], acc);
+    }
+  }
+  const float out = tot > 0.0f ? acc / tot : 0.0f;
+  uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1];
+  Op[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
+  if (p.lse != nullptr && d == 0)
+    p.lse[(long long)b * p.Hq + hq] = tot > 0.0f ? (m + __log2f(tot)) * kLn2 : -INFINITY;
+}
+
+template <int D, int G>
+struct LaunchDecode {
+  const DecodeParams& P;
+  hipStream_t stream;
+  template <class Score>
+  void operator()() {
+    dim3 grid(P.splits, P.f.Hkv, P.f.B);
+    hipLaunchKernelGGL((decode_partial_kernel<D, G, Score>), grid, dim3(kDecThreads), 0, stream, P);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(P.f.B * P.f.Hq), dim3(D), 0, stream, P);
+  }
+};
+
+template <int D, int G>
+bool launch_dg(int score_kind, const DecodeParams& P, hipStream_t stream) {
+  LaunchDecode<D, G> l{P, stream};
+  return dispatch_score(score_kind, l);
+}
+
+template <int D>
+bool launch_d(int G, int score_kind, const DecodeParams& P, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_dg<D, 1>(score_kind, P, stream);
+    case 2: return launch_dg<D, 2>(score_kind, P, stream);
+    case 4: return launch_dg<D, 4>(score_kind, P, stream);
+    case 8: return launch_dg<D, 8>(score_kind, P, stream);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+fa_status launch_decode(int D, int G, int score_kind, const DecodeParams& P, hipStream_t stream) {
+  bool ok;
+  if (D == 128)
+    ok = launch_d<128>(G, score_kind, P, stream);
+  else if (D == 64)
+    ok = launch_d<64>(G, score_kind, P, stream);
+  else
+    return FA_ERR_UNSUPPORTED;
+  if (!ok) return FA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int decode_max_blocks_per_split() { return kMaxBps; }
+
+}  // namespace fa

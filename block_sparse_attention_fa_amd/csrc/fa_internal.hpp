@@ -1,0 +1,90 @@
+// Internal declarations shared by the host dispatch (fa_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+
+namespace fa {
+
+// Runtime parameters of the mask_mods (see fa_mask_desc).
+struct MaskParams {
+  int window;
+  int prefix_len;
+  const int* doc;
+  long long doc_stride_b;
+  const int* kv_len;
+};
+
+// Runtime parameters of the score_mods, with host-folded constants.
+// Scores inside the kernels are kept in base-2 units: x2 = mod(s) * log2(e),
+// so that the softmax exponentials are single exp2 instructions.
+struct ScoreParams {
+  float scale;        // 1/sqrt(D) unless given
+  float scale_log2;   // scale * log2(e)
+  float cap_log2;     // softcap * log2(e)
+  float tanh_k;       // 2 * scale / softcap * log2(e): exp2 argument of tanh's identity
+  const float* slopes;  // ALiBi slopes [Hq] or nullptr (default geometric slopes)
+  int Hq;
+  const uint16_t* bias;
+  long long bs0, bs1, bs2;  // bias strides for b, h, q (kv stride is 1)
+};
+
+struct BlockMaskView {
+  const int* kv_num;
+  const int* kv_idx;
+  const int* full_num;
+  const int* full_idx;
+  int Bm, Hm, NQ, NK;
+  int dense;          // no BlockMask: every kv tile is treated as full
+  int separate_full;  // 0: kv_* already holds every non-empty tile
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  long long qs[4], ks[4], vs[4], os[4];
+  int B, Hq, Hkv, Sq, Skv, G;
+  BlockMaskView bm;
+  MaskParams mask;
+  ScoreParams score;
+};
+
+struct DecodeParams {
+  FwdParams f;          // Sq == 1
+  int mask_kind;        // decode evaluates the mask through a runtime switch
+  int splits;           // splits per (b, hkv) row = grid.x
+  int blocks_per_split; // kv tiles per split
+  float* ws_o;          // [B, Hq, splits, D] fp32 (normalised partial outputs)
+  float* ws_lse;        // [B, Hq, splits] fp32 base-2 LSE of each split
+};
+
+struct BuildParams {
+  int* kv_num;
+  int* kv_idx;
+  int* full_num;
+  int* full_idx;
+  int Bm, Hm, NQ, NK, Sq, Skv;
+  int separate_full;
+  MaskParams mask;
+};
+
+fa_status launch_block_mask(int mask_kind, const BuildParams& p, hipStream_t stream);
+fa_status launch_forward(int D, int mask_kind, int score_kind, const FwdParams& p, hipStream_t stream);
+// One translation unit per mask kind (compiled in parallel).
+fa_status launch_forward_none(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_causal(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_window(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_sliding_causal(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_document(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_document_causal(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_prefix_lm(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_forward_kv_len(int D, int score_kind, const FwdParams& p, hipStream_t stream);
+fa_status launch_decode(int D, int G, int score_kind, const DecodeParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,8 @@
+// Forward instantiations for the MaskSlidingCausal mask_mod (every score_mod, D = 64 and 128).
+#include "fwd_kernel.hpp"
+
+namespace fa {
+fa_status launch_forward_sliding_causal(int D, int score_kind, const FwdParams& p, hipStream_t stream) {
+  return launch_forward_mask<MaskSlidingCausal>(D, score_kind, p, stream);
+}
+}  // namespace fa

@@ -1,0 +1,234 @@
+// Compile-time mask_mod and score_mod functors.
+//
+// A mask_mod decides from positions alone whether a query attends to a key
+// (attention-gym "Concepts" page, "mask_mod"); a score_mod rewrites the scaled
+// score (Concepts, "score_mod"; paper review "Flex Attention: A Programming
+// Model for Generating Optimized Attention Kernels", §2.1-2.2).  Both are
+// written once here and instantiated into the builder, forward and decode
+// kernels; their runtime parameters (window, prefix, document ids, lengths,
+// slopes, cap, bias tensor) are kernel arguments, so changing them never needs
+// a rebuild.
+//
+// Every functor is split into a per-query-row part (`row`) evaluated once per
+// lane and a per-key part evaluated per element, because each lane of the
+// kernels owns one query row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.hpp"
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---------------------------------------------------------------------------
+// mask_mods
+// ---------------------------------------------------------------------------
+
+struct MaskNone {
+  static constexpr bool kBatchDependent = false;
+  struct Row {
+    __device__ __forceinline__ bool operator()(int) const { return true; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams&, int, int, int) { return {}; }
+};
+
+// Concepts "mask_mod": causal, q >= kv.
+struct MaskCausal {
+  static constexpr bool kBatchDependent = false;
+  struct Row {
+    int q;
+    __device__ __forceinline__ bool operator()(int kv) const { return q >= kv; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams&, int, int, int q) { return {q}; }
+};
+
+// The window term of Concepts "Composing masks": q - kv <= window.
+struct MaskWindow {
+  static constexpr bool kBatchDependent = false;
+  struct Row {
+    int lo;  // smallest kv with q - kv <= window
+    __device__ __forceinline__ bool operator()(int kv) const { return kv >= lo; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int, int, int q) {
+    return {q - p.window};
+  }
+};
+
+// Talk summary (variant list) / paper review §5.3: same document only.
+struct MaskDocument {
+  static constexpr bool kBatchDependent = true;
+  struct Row {
+    const int* doc;
+    int dq;
+    __device__ __forceinline__ bool operator()(int kv) const { return doc[kv] == dq; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int b, int, int q) {
+    const int* d = p.doc + (long long)b * p.doc_stride_b;
+    return {d, d[q]};
+  }
+};
+
+// The prefix term of paper review §4.4: keys before prefix_len are visible to all.
+struct MaskPrefix {
+  static constexpr bool kBatchDependent = false;
+  struct Row {
+    int n;
+    __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int, int, int) { return {p.prefix_len}; }
+};
+
+// Valid prefix of a KV cache: kv < kv_len[b].
+struct MaskKvLen {
+  static constexpr bool kBatchDependent = true;
+  struct Row {
+    int n;
+    __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int b, int, int) { return {p.kv_len[b]}; }
+};
+
+// Logical fusion (paper review §4.4; Concepts "Composing masks").
+template <class A, class B>
+struct MaskAnd {
+  static constexpr bool kBatchDependent = A::kBatchDependent || B::kBatchDependent;
+  struct Row {
+    typename A::Row a;
+    typename B::Row b;
+    __device__ __forceinline__ bool operator()(int kv) const { return a(kv) && b(kv); }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int b, int h, int q) {
+    return {A::row(p, b, h, q), B::row(p, b, h, q)};
+  }
+};
+
+template <class A, class B>
+struct MaskOr {
+  static constexpr bool kBatchDependent = A::kBatchDependent || B::kBatchDependent;
+  struct Row {
+    typename A::Row a;
+    typename B::Row b;
+    __device__ __forceinline__ bool operator()(int kv) const { return a(kv) || b(kv); }
+  };
+  static __device__ __forceinline__ Row row(const MaskParams& p, int b, int h, int q) {
+    return {A::row(p, b, h, q), B::row(p, b, h, q)};
+  }
+};
+
+using MaskSlidingCausal = MaskAnd<MaskCausal, MaskWindow>;
+using MaskDocumentCausal = MaskAnd<MaskDocument, MaskCausal>;
+using MaskPrefixLM = MaskOr<MaskPrefix, MaskCausal>;
+
+// Calls f.template operator()<MaskType>() for a runtime fa_mask_kind.
+template <class F>
+__host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
+  switch (kind) {
+    case FA_MASK_NONE: f.template operator()<MaskNone>(); return true;
+    case FA_MASK_CAUSAL: f.template operator()<MaskCausal>(); return true;
+    case FA_MASK_SLIDING_WINDOW: f.template operator()<MaskWindow>(); return true;
+    case FA_MASK_SLIDING_CAUSAL: f.template operator()<MaskSlidingCausal>(); return true;
+    case FA_MASK_DOCUMENT: f.template operator()<MaskDocument>(); return true;
+    case FA_MASK_DOCUMENT_CAUSAL: f.template operator()<MaskDocumentCausal>(); return true;
+    case FA_MASK_PREFIX_LM: f.template operator()<MaskPrefixLM>(); return true;
+    case FA_MASK_KV_LEN: f.template operator()<MaskKvLen>(); return true;
+    default: return false;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// score_mods, producing base-2 scores x2 = mod(s) * log2(e).
+//
+// `s` is the raw dot product Q.K (not yet scaled).  apply4 handles four
+// consecutive keys kv0..kv0+3 of one query row; `Tile` carries values a
+// functor wants loaded before the score matrix is ready (the bias tensor).
+// ---------------------------------------------------------------------------
+
+struct ScoreNone {
+  struct Row {
+    float c;
+  };
+  struct Tile {};
+  static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) { return {p.scale_log2}; }
+  static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) { return s * r.c; }
+};
+
+// Concepts "score_mod": s + slope[h] * (kv - q).
+struct ScoreAlibi {
+  struct Row {
+    float c;    // scale * log2e
+    float sl;   // slope[h] * log2e
+    int q;
+  };
+  static __device__ __forceinline__ Row row(const ScoreParams& p, int, int h, int q) {
+    float slope = p.slopes ? p.slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)p.Hq);
+    return {p.scale_log2, slope * kLog2e, q};
+  }
+  static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
+    return fmaf(s, r.c, r.sl * (float)(kv - r.q));
+  }
+};
+
+// Softcapping (paper review §2.1 table): cap * tanh(s / cap), with
+// tanh(y) = 1 - 2 / (1 + e^{2y}) evaluated with the hardware exp2 and
+// reciprocal; the error this adds is measured against fp64 tanh in the tests.
+struct ScoreSoftcap {
+  struct Row {
+    float k;     // 2 * scale / cap * log2e
+    float c2;    // cap * log2e
+  };
+  static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) {
+    return {p.tanh_k, p.cap_log2};
+  }
+  static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) {
+    float e = __builtin_amdgcn_exp2f(s * r.k);
+    return fmaf(-2.0f * r.c2, __builtin_amdgcn_rcpf(1.0f + e), r.c2);
+  }
+};
+
+// Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
+struct ScoreRelPos {
+  struct Row {
+    float c;
+    int q;
+  };
+  static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int q) { return {p.scale_log2, q}; }
+  static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
+    return fmaf(s, r.c, kLog2e * (float)(r.q - kv));
+  }
+};
+
+// Dynamic-bias feature request (attention-gym issue 123): s + bias[b,h,q,kv].
+struct ScoreBias {
+  struct Row {
+    float c;
+    const uint16_t* row;  // bias[b, h, q, :]
+  };
+  static __device__ __forceinline__ Row row(const ScoreParams& p, int b, int h, int q) {
+    return {p.scale_log2, p.bias + (long long)b * p.bs0 + (long long)h * p.bs1 + (long long)q * p.bs2};
+  }
+  static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
+    return fmaf(kLog2e, bf16_bits_to_float(r.row[kv]), s * r.c);
+  }
+};
+
+template <class F>
+__host__ __device__ inline bool dispatch_score(int kind, F&& f) {
+  switch (kind) {
+    case FA_SCORE_NONE: f.template operator()<ScoreNone>(); return true;
+    case FA_SCORE_ALIBI: f.template operator()<ScoreAlibi>(); return true;
+    case FA_SCORE_SOFTCAP: f.template operator()<ScoreSoftcap>(); return true;
+    case FA_SCORE_REL_POS: f.template operator()<ScoreRelPos>(); return true;
+    case FA_SCORE_BIAS: f.template operator()<ScoreBias>(); return true;
+    default: return false;
+  }
+}
+
+}  // namespace fa

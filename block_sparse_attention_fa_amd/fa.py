@@ -1,0 +1,276 @@
+"""Thin ctypes binding of libfa.so (include/fa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the current
+stream.  The functions keep the C names:
+
+    fa_block_mask_dims, fa_build_block_mask, fa_forward,
+    fa_decode_workspace_size, fa_decode
+
+plus small helpers to describe mask_mods / score_mods and to inspect a
+BlockMask (ASCII print and sparsity, as on the attention-gym "Concepts"
+page, "Inspecting a BlockMask").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+# --- enums (include/fa.h) ----------------------------------------------------
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
+FA_BLOCK = 128
+
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_SLIDING_CAUSAL = 0, 1, 2, 3
+MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL, MASK_PREFIX_LM, MASK_KV_LEN = 4, 5, 6, 7
+SCORE_NONE, SCORE_ALIBI, SCORE_SOFTCAP, SCORE_REL_POS, SCORE_BIAS = 0, 1, 2, 3, 4
+
+MASK_KINDS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding_window": MASK_SLIDING_WINDOW,
+              "sliding_causal": MASK_SLIDING_CAUSAL, "document": MASK_DOCUMENT,
+              "document_causal": MASK_DOCUMENT_CAUSAL, "prefix_lm": MASK_PREFIX_LM, "kv_len": MASK_KV_LEN}
+SCORE_KINDS = {"none": SCORE_NONE, "alibi": SCORE_ALIBI, "softcap": SCORE_SOFTCAP,
+               "rel_pos": SCORE_REL_POS, "bias": SCORE_BIAS}
+
+
+class MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("window", c_int32), ("prefix_len", c_int32), ("reserved0", c_int32),
+                ("doc_ids", c_void_p), ("doc_stride_b", c_int64), ("kv_len", c_void_p)]
+
+
+class ScoreDesc(ctypes.Structure):
+    _fields_ = [("kind", c_int32), ("softcap", c_float), ("alibi_slopes", c_void_p),
+                ("bias", c_void_p), ("bias_stride", c_int64 * 4)]
+
+
+class BlockMaskC(ctypes.Structure):
+    _fields_ = [("kv_num_blocks", c_void_p), ("kv_indices", c_void_p),
+                ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p),
+                ("Bm", c_int32), ("Hm", c_int32), ("NQ", c_int32), ("NK", c_int32),
+                ("block_q", c_int32), ("block_kv", c_int32), ("separate_full", c_int32),
+                ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o", c_void_p), ("lse", c_void_p),
+                ("q_stride", c_int64 * 4), ("k_stride", c_int64 * 4), ("v_stride", c_int64 * 4),
+                ("o_stride", c_int64 * 4),
+                ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("Sq", c_int32), ("Skv", c_int32),
+                ("D", c_int32), ("scale", c_float), ("block_mask", POINTER(BlockMaskC)),
+                ("score", ScoreDesc), ("num_splits", c_int32)]
+
+
+# symbol -> (restype, argtypes)
+SIGNATURES = {
+    "fa_abi_version": (c_int32, []),
+    "fa_status_string": (c_char_p, [c_int32]),
+    "fa_last_error": (c_char_p, []),
+    "fa_block_mask_dims": (c_int32, [c_int32, c_int32, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]),
+    "fa_build_block_mask": (c_int32, [POINTER(BlockMaskC), c_int32, c_int32, c_void_p]),
+    "fa_forward": (c_int32, [POINTER(AttnArgs), c_void_p]),
+    "fa_decode_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
+    "fa_decode": (c_int32, [POINTER(AttnArgs), c_void_p, c_size_t, c_void_p]),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libfa.so.  Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_sparse_attention_fa_amd._build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int):
+    if status != FA_OK:
+        L = lib()
+        raise FAError(status, f"{L.fa_status_string(status).decode()}: {L.fa_last_error().decode()}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+# --- descriptors ---------------------------------------------------------------
+
+class MaskMod:
+    """A mask_mod kind with its runtime parameters (tensors stay referenced here)."""
+
+    def __init__(self, kind="none", window=0, prefix_len=0, doc_ids=None, kv_len=None):
+        self.kind = MASK_KINDS[kind] if isinstance(kind, str) else int(kind)
+        self.window, self.prefix_len = int(window), int(prefix_len)
+        self.doc_ids, self.kv_len = doc_ids, kv_len
+
+    def desc(self) -> MaskDesc:
+        d = MaskDesc()
+        d.kind, d.window, d.prefix_len = self.kind, self.window, self.prefix_len
+        if self.doc_ids is not None:
+            d.doc_ids = self.doc_ids.data_ptr()
+            d.doc_stride_b = self.doc_ids.stride(0) if self.doc_ids.dim() == 2 and self.doc_ids.shape[0] > 1 else 0
+        if self.kv_len is not None:
+            d.kv_len = self.kv_len.data_ptr()
+        return d
+
+
+class ScoreMod:
+    """A score_mod kind with its runtime parameters."""
+
+    def __init__(self, kind="none", softcap=0.0, alibi_slopes=None, bias=None):
+        self.kind = SCORE_KINDS[kind] if isinstance(kind, str) else int(kind)
+        self.softcap, self.alibi_slopes, self.bias = float(softcap), alibi_slopes, bias
+
+    def desc(self) -> ScoreDesc:
+        d = ScoreDesc()
+        d.kind, d.softcap = self.kind, self.softcap
+        if self.alibi_slopes is not None:
+            d.alibi_slopes = self.alibi_slopes.data_ptr()
+        if self.bias is not None:
+            d.bias = self.bias.data_ptr()
+            for i, s in enumerate(self.bias.stride()):
+                d.bias_stride[i] = s if (self.bias.shape[i] > 1 or i == 3) else 0
+        return d
+
+
+class BlockMask:
+    """Device BlockMask: the four int32 tensors of the Concepts page's "Key attributes"."""
+
+    def __init__(self, mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda"):
+        import torch
+        NQ, NK = fa_block_mask_dims(Sq, Skv)
+        self.mask = mask
+        self.Bm, self.Hm, self.NQ, self.NK, self.Sq, self.Skv = Bm, Hm, NQ, NK, Sq, Skv
+        self.separate_full = bool(separate_full)
+        z = dict(dtype=torch.int32, device=device)
+        self.kv_num_blocks = torch.empty((Bm, Hm, NQ), **z)
+        self.kv_indices = torch.empty((Bm, Hm, NQ, NK), **z)
+        self.full_kv_num_blocks = torch.empty((Bm, Hm, NQ), **z)
+        self.full_kv_indices = torch.empty((Bm, Hm, NQ, NK), **z)
+        self.c = BlockMaskC()
+        c = self.c
+        c.kv_num_blocks, c.kv_indices = self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr()
+        c.full_kv_num_blocks, c.full_kv_indices = self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr()
+        c.Bm, c.Hm, c.NQ, c.NK = Bm, Hm, NQ, NK
+        c.block_q = c.block_kv = FA_BLOCK
+        c.separate_full = 1 if separate_full else 0
+        c.mask = mask.desc()
+
+    def tensors(self):
+        return {"kv_num_blocks": self.kv_num_blocks, "kv_indices": self.kv_indices,
+                "full_kv_num_blocks": self.full_kv_num_blocks, "full_kv_indices": self.full_kv_indices}
+
+    def classes(self):
+        """int8 [Bm,Hm,NQ,NK] on the host: 0 empty, 1 partial, 2 full (decoded from the lists)."""
+        import numpy as np
+        kn = self.kv_num_blocks.cpu().numpy()
+        ki = self.kv_indices.cpu().numpy()
+        fn = self.full_kv_num_blocks.cpu().numpy()
+        fi = self.full_kv_indices.cpu().numpy()
+        cls = np.zeros((self.Bm, self.Hm, self.NQ, self.NK), dtype=np.int8)
+        for idx in np.ndindex(self.Bm, self.Hm, self.NQ):
+            cls[idx][ki[idx][:kn[idx]]] = 1
+            cls[idx][fi[idx][:fn[idx]]] = 2
+        return cls
+
+    def sparsity(self) -> float:
+        """Percentage of tiles that are empty (Concepts, "Inspecting a BlockMask")."""
+        cls = self.classes()
+        return 100.0 * float((cls == 0).sum()) / float(cls.size)
+
+    def to_string(self, b=0, h=0) -> str:
+        """ASCII picture: full '██', partial '░░', empty blank."""
+        glyph = {2: "██", 1: "░░", 0: "  "}
+        return "\n".join("".join(glyph[int(x)] for x in row).rstrip() for row in self.classes()[b, h])
+
+    __str__ = to_string
+
+
+# --- entry points (same names as the C ABI) ---------------------------------------
+
+def fa_block_mask_dims(Sq, Skv, block_q=FA_BLOCK, block_kv=FA_BLOCK):
+    nq, nk = c_int32(), c_int32()
+    _check(lib().fa_block_mask_dims(Sq, Skv, block_q, block_kv, ctypes.byref(nq), ctypes.byref(nk)))
+    return nq.value, nk.value
+
+
+def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", stream=None):
+    """Allocate a BlockMask and build it on the device (asynchronously on `stream`)."""
+    bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device)
+    _check(lib().fa_build_block_mask(ctypes.byref(bm.c), Sq, Skv, _stream(stream)))
+    return bm
+
+
+def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits):
+    a = AttnArgs()
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    a.lse = lse.data_ptr() if lse is not None else None
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        arr = getattr(a, name)
+        for i, s in enumerate(t.stride()):
+            arr[i] = s
+    a.B, a.Hq, a.Sq, a.D = q.shape
+    a.Hkv, a.Skv = k.shape[1], k.shape[2]
+    a.scale = float(scale)
+    a.block_mask = ctypes.pointer(block_mask.c) if block_mask is not None else None
+    a.score = (score or ScoreMod()).desc()
+    a.num_splits = int(num_splits)
+    return a
+
+
+def fa_forward(q, k, v, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
+               scale=0.0, out=None, lse=None, stream=None):
+    """O = softmax(mod(Q K^T * scale)) V for bf16 Q [B,Hq,Sq,D], K/V [B,Hkv,Skv,D]."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    a = _attn_args(q, k, v, out, lse, block_mask, score, scale, 0)
+    _check(lib().fa_forward(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def fa_decode_workspace_size(q, k, v, block_mask=None, score=None, num_splits=0):
+    a = _attn_args(q, k, v, q, None, block_mask, score, 0.0, num_splits)
+    n = c_size_t()
+    _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
+              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D]."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits)
+    n = c_size_t()
+    _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(1, n.value // 4), dtype=torch.float32, device=q.device)
+    _check(lib().fa_decode(ctypes.byref(a), c_void_p(workspace.data_ptr()),
+                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

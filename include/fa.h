@@ -1,0 +1,205 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) block-sparse FlexAttention library (libfa.so).
+ *
+ * What the library computes is fixed by the FlexAttention pages:
+ *   O = softmax(mod(Q K^T / sqrt(d))) V
+ * (paper review "Flex Attention: A Programming Model for Generating Optimized
+ * Attention Kernels", §2.1), where the mod is a score_mod applied to the
+ * scaled score and a mask_mod that removes positions (attention-gym
+ * "Concepts" page, sections "mask_mod", "score_mod", "When to use which?").
+ * Masked positions count as -inf; the score_mod is only applied where the
+ * mask keeps the position.  Work is skipped per 128x128 tile through a
+ * BlockMask (Concepts, "BlockMask Internals" and "Key attributes"; paper
+ * review §4.1-4.3).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates and frees no memory; decode's workspace is caller-provided.
+ *  - bfloat16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous and ordered on that stream.
+ *  - Arguments are validated on the host before any HIP call; a failed
+ *    check returns a status and launches nothing.  fa_last_error() then
+ *    returns a message naming the failed check (per calling thread).
+ *  - Launch failures return FA_ERR_HIP.  Faults inside a kernel surface at
+ *    the caller's next synchronisation, as for any HIP kernel.
+ *  - No global mutable state (the last-error message is per thread): calls
+ *    may be made from several threads at once.
+ *  - Changing any runtime parameter (window, prefix length, document ids,
+ *    lengths, slopes, cap, bias tensor, BlockMask contents) never needs a
+ *    rebuild: only the mask/score *kind* selects compiled code (Concepts,
+ *    "Changing BlockMask doesn't require recompilation"; the dynamic-bias
+ *    feature request, attention-gym issue 123).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+#define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* sizes, strides or BlockMask dims are inconsistent */
+  FA_ERR_UNSUPPORTED = 3, /* valid request outside what is compiled (D, block size, kind, alignment) */
+  FA_ERR_WORKSPACE = 4,   /* decode workspace missing or too small */
+  FA_ERR_HIP = 5          /* a HIP launch failed */
+} fa_status;
+
+/* mask_mod kinds (Concepts "mask_mod" / "Composing masks"; paper review §2.2, §4.4;
+ * talk summary "FlexAttention: A Flexible and Performant Approach to Transformer
+ * Attention", variant list).  q and kv are absolute token indices; b is the batch row. */
+typedef enum {
+  FA_MASK_NONE = 0,            /* every position attends */
+  FA_MASK_CAUSAL = 1,          /* q >= kv */
+  FA_MASK_SLIDING_WINDOW = 2,  /* q - kv <= window (the window term alone) */
+  FA_MASK_SLIDING_CAUSAL = 3,  /* AND(causal, window): 0 <= q - kv <= window */
+  FA_MASK_DOCUMENT = 4,        /* doc[b][q] == doc[b][kv] */
+  FA_MASK_DOCUMENT_CAUSAL = 5, /* AND(document, causal) */
+  FA_MASK_PREFIX_LM = 6,       /* OR(kv < prefix_len, causal) */
+  FA_MASK_KV_LEN = 7,          /* kv < kv_len[b] (valid prefix of a KV cache) */
+  FA_MASK_KIND_COUNT = 8
+} fa_mask_kind;
+
+typedef struct {
+  int32_t kind;            /* fa_mask_kind */
+  int32_t window;          /* SLIDING_*: inclusive window, >= 0 */
+  int32_t prefix_len;      /* PREFIX_LM: keys [0, prefix_len) are visible to every query, >= 0 */
+  int32_t reserved0;
+  const int32_t* doc_ids;  /* DOCUMENT*: device int32; token t of batch row b has id
+                              doc_ids[b * doc_stride_b + t]; shared by queries and keys, so
+                              these kinds need Sq == Skv */
+  int64_t doc_stride_b;    /* elements; 0 = one layout for every batch row */
+  const int32_t* kv_len;   /* KV_LEN: device int32 [B] valid lengths */
+} fa_mask_desc;
+
+/* score_mod kinds (Concepts "score_mod"; paper review §2.1 table; talk summary;
+ * dynamic-bias feature request).  `s` is the scaled score Q.K * scale. */
+typedef enum {
+  FA_SCORE_NONE = 0,    /* s */
+  FA_SCORE_ALIBI = 1,   /* s + slope[h] * (kv - q) */
+  FA_SCORE_SOFTCAP = 2, /* softcap * tanh(s / softcap) */
+  FA_SCORE_REL_POS = 3, /* s + (q - kv) */
+  FA_SCORE_BIAS = 4,    /* s + bias[b, h, q, kv] (bf16 tensor, read per element) */
+  FA_SCORE_KIND_COUNT = 5
+} fa_score_kind;
+
+typedef struct {
+  int32_t kind;                /* fa_score_kind */
+  float softcap;               /* SOFTCAP: cap > 0 */
+  const float* alibi_slopes;   /* ALIBI: device fp32 [Hq], or NULL for slope[h] = 2^(-8(h+1)/Hq) */
+  const uint16_t* bias;        /* BIAS: device bf16; element (b,h,q,kv) at
+                                  b*s[0] + h*s[1] + q*s[2] + kv*s[3] */
+  int64_t bias_stride[4];      /* elements, >= 0; 0 broadcasts a dim; s[3] must be 1 */
+} fa_score_desc;
+
+/* BlockMask (Concepts "Key attributes"; paper review §4.1).  All four index
+ * tensors are caller-allocated device int32, written by fa_build_block_mask:
+ *   kv_num_blocks [Bm,Hm,NQ], kv_indices [Bm,Hm,NQ,NK],
+ *   full_kv_num_blocks [Bm,Hm,NQ], full_kv_indices [Bm,Hm,NQ,NK],
+ * contiguous, NQ = ceil(Sq/128), NK = ceil(Skv/128).  Lists are ascending and
+ * padded with 0.  With separate_full = 1 (canonical) kv_* lists the partial
+ * tiles and full_* the full tiles (disjoint); with separate_full = 0, kv_*
+ * lists every non-empty tile and full_* the full ones among them, and the
+ * forward then evaluates the mask on every listed tile.  A tile is full when
+ * every in-range position attends, empty when none does (Concepts,
+ * "BlockMask Internals"; paper review §4.2).  Bm is 1 or B and Hm is 1 or Hq;
+ * a dim of 1 is shared by every batch row / head.  The mask descriptor is
+ * carried with the tensors and is evaluated on partial tiles. */
+typedef struct {
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+  int32_t Bm, Hm, NQ, NK;
+  int32_t block_q, block_kv; /* must both be FA_BLOCK */
+  int32_t separate_full;     /* 1 = disjoint lists (canonical), 0 = superset */
+  int32_t Sq, Skv;           /* set by fa_build_block_mask; fa_forward checks them */
+  fa_mask_desc mask;
+} fa_block_mask;
+
+/* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]
+ * (for decode: the KV cache, Skv = its capacity).  Strides are in elements
+ * for dims (b, h, s, d); the d stride must be 1, other strides multiples of 8,
+ * base pointers 16-byte aligned.  GQA: query head hq reads KV head
+ * hq / (Hq / Hkv) (paper review §3.3 lists GQA support). */
+typedef struct {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;                 /* optional fp32 [B,Hq,Sq] contiguous, natural-log LSE; -inf for empty rows */
+  int64_t q_stride[4], k_stride[4], v_stride[4], o_stride[4];
+  int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128} */
+  float scale;                /* 0 => 1/sqrt(D) */
+  const fa_block_mask* block_mask; /* NULL => dense attention without a mask */
+  fa_score_desc score;
+  int32_t num_splits;         /* decode: max KV splits per sequence, 0 = auto; ignored by fa_forward */
+} fa_attn_args;
+
+/* Version of this ABI (FA_ABI_VERSION). */
+int32_t fa_abi_version(void);
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* fa_status_string(fa_status s);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char* fa_last_error(void);
+
+/* Host only.  NQ = ceil(Sq/block_q), NK = ceil(Skv/block_kv).
+ * Errors: NULL outputs, sizes <= 0, a block size other than FA_BLOCK. */
+fa_status fa_block_mask_dims(int32_t Sq, int32_t Skv, int32_t block_q, int32_t block_kv,
+                             int32_t* NQ, int32_t* NK);
+
+/* Build a BlockMask on the device (Concepts "BlockMask Internals": every
+ * 128x128 tile is classified full / partial / empty from the mask_mod, then
+ * compacted into the four index tensors).  `bm` is host memory with the four
+ * device pointers, Bm, Hm, NQ, NK, block sizes, separate_full and the mask
+ * descriptor filled in; on success bm->Sq and bm->Skv are set.  Every entry
+ * of the four tensors is written (padding included).  The mask is evaluated
+ * for b' < Bm and h' < Hm.
+ * Errors: FA_ERR_NULL (tensor pointers, doc_ids/kv_len needed by the kind),
+ * FA_ERR_SHAPE (NQ/NK not matching Sq/Skv, Bm or Hm < 1, Sq != Skv for a
+ * document kind, negative window/prefix), FA_ERR_UNSUPPORTED (block size,
+ * unknown kind), FA_ERR_HIP. */
+fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* stream);
+
+/* Fused block-sparse attention forward (paper review §2.1, §3.3, §4.2-4.3):
+ * for each (b, hq, 128-row query tile) one workgroup walks the tile's
+ * partial list (mask evaluated per element) and then its full list (no mask),
+ * with online softmax, writing O (bf16) and optionally LSE.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (sizes, Hq % Hkv, strides, BlockMask dims,
+ * Bm/Hm not in {1,B}/{1,Hq}, a batch-dependent mask with Bm = 1 < B, a BlockMask
+ * built for other lengths), FA_ERR_UNSUPPORTED (D, alignment, kinds, bias
+ * stride[3] != 1), FA_ERR_HIP. */
+fa_status fa_forward(const fa_attn_args* a, void* stream);
+
+/* Host only.  Bytes of decode workspace fa_decode needs for these arguments
+ * (fp32 partial outputs and LSEs of every split).  Same validation as fa_decode. */
+fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
+
+/* Split-KV decode (talk summary, "Flex Decoding": split along the key axis
+ * for parallelism, then a final reduction; score_mod still applies).  Sq must
+ * be 1; the query sits at q index 0.  Each sequence's block list (its
+ * BlockMask row) is cut into chunks; one workgroup per (chunk, KV head, batch
+ * row) computes all Hq/Hkv query heads of that KV head against the chunk, and
+ * a merge kernel combines the chunks through their log-sum-exp.  The result
+ * does not depend on the split count beyond fp32 rounding.  The GQA group
+ * size Hq/Hkv must be 1, 2, 4 or 8, and 1 when Hm > 1.  num_splits (0 = auto)
+ * sets how many chunks a sequence is cut into; a chunk holds 1 to 8 tiles, so
+ * the split count used is ceil(NK / clamp(ceil(NK / num_splits), 1, 8)).
+ * Errors: as fa_forward, plus FA_ERR_SHAPE for Sq != 1 and FA_ERR_WORKSPACE. */
+fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: libfa.so loads, exports every function include/fa.h
+declares, and host-side validation rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_fa_amd import fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"fa_build_block_mask", "fa_forward", "fa_decode", "fa_decode_workspace_size",
+            "fa_block_mask_dims", "fa_status_string", "fa_last_error", "fa_abi_version"} <= set(names)
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
+    assert set(names) == set(fa.SIGNATURES), "binding signatures out of sync with fa.h"
+
+
+def test_abi_version_and_status_strings():
+    L = fa.lib()
+    assert L.fa_abi_version() == 1
+    for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
+                                 "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
+        assert L.fa_status_string(code).decode() == name
+
+
+def test_block_mask_dims():
+    assert fa.fa_block_mask_dims(256, 256) == (2, 2)
+    assert fa.fa_block_mask_dims(300, 1) == (3, 1)
+    assert fa.fa_block_mask_dims(8192, 16384) == (64, 128)
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_block_mask_dims(256, 256, 64, 64)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_block_mask_dims(0, 256)
+    assert e.value.status == fa.FA_ERR_SHAPE
+
+
+def _args(B=1, Hq=2, Hkv=2, Sq=256, Skv=256, D=64, ptr=0x10000):
+    a = fa.AttnArgs()
+    a.q = a.k = a.v = a.o = ptr
+    for name, (H, S) in (("q_stride", (Hq, Sq)), ("k_stride", (Hkv, Skv)), ("v_stride", (Hkv, Skv)),
+                         ("o_stride", (Hq, Sq))):
+        st = getattr(a, name)
+        st[0], st[1], st[2], st[3] = H * S * D, S * D, D, 1
+    a.B, a.Hq, a.Hkv, a.Sq, a.Skv, a.D = B, Hq, Hkv, Sq, Skv, D
+    return a
+
+
+def _status(a, decode=False):
+    L = fa.lib()
+    if decode:
+        n = ctypes.c_size_t()
+        return L.fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return L.fa_forward(ctypes.byref(a), None)
+
+
+def test_forward_validation_codes():
+    a = _args(); a.q = None
+    assert _status(a) == fa.FA_ERR_NULL
+    a = _args(Hq=3, Hkv=2)
+    assert _status(a) == fa.FA_ERR_SHAPE
+    a = _args(D=96)
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED
+    a = _args(); a.q_stride[3] = 2
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED
+    a = _args(); a.q = 0x10008  # not 16-byte aligned
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED
+    a = _args(); a.score.kind = 9
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED
+    a = _args(); a.score.kind = fa.SCORE_SOFTCAP; a.score.softcap = 0.0
+    assert _status(a) == fa.FA_ERR_SHAPE
+    a = _args(); a.score.kind = fa.SCORE_BIAS
+    assert _status(a) == fa.FA_ERR_NULL
+    a = _args(); a.B = 0
+    assert _status(a) == fa.FA_ERR_SHAPE
+    assert "sizes must be positive" in fa.lib().fa_last_error().decode()
+
+
+def _bm(Bm=1, Hm=1, NQ=2, NK=2, kind=fa.MASK_CAUSAL, Sq=256, Skv=256):
+    b = fa.BlockMaskC()
+    b.kv_num_blocks = b.kv_indices = b.full_kv_num_blocks = b.full_kv_indices = 0x10000
+    b.Bm, b.Hm, b.NQ, b.NK = Bm, Hm, NQ, NK
+    b.block_q = b.block_kv = 128
+    b.separate_full = 1
+    b.Sq, b.Skv = Sq, Skv
+    b.mask.kind = kind
+    return b
+
+
+def test_blockmask_validation_codes():
+    L = fa.lib()
+    b = _bm(NQ=3)
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_SHAPE
+    b = _bm(); b.block_q = 64
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_UNSUPPORTED
+    b = _bm(kind=fa.MASK_DOCUMENT)
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_NULL
+    b = _bm(kind=fa.MASK_SLIDING_CAUSAL); b.mask.window = -1
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_SHAPE
+    b = _bm(kind=fa.MASK_KV_LEN)
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_NULL
+    b = _bm(); b.kv_indices = None
+    assert L.fa_build_block_mask(None, 256, 256, None) == fa.FA_ERR_NULL
+    assert L.fa_build_block_mask(ctypes.byref(b), 256, 256, None) == fa.FA_ERR_NULL
+    # the forward rejects a BlockMask built for other lengths, or with a bad broadcast
+    a = _args(B=2); b = _bm(Sq=200)
+    a.block_mask = ctypes.pointer(b)
+    assert _status(a) == fa.FA_ERR_SHAPE
+    a = _args(B=2); b = _bm(Bm=3)
+    a.block_mask = ctypes.pointer(b)
+    assert _status(a) == fa.FA_ERR_SHAPE
+    a = _args(B=2); b = _bm(kind=fa.MASK_KV_LEN); b.mask.kv_len = 0x10000
+    a.block_mask = ctypes.pointer(b)
+    assert _status(a) == fa.FA_ERR_SHAPE  # batch-dependent mask with Bm = 1 < B
+    a = _args(); b = _bm(kind=fa.MASK_DOCUMENT, Skv=300, NK=3); b.mask.doc_ids = 0x10000
+    a.Skv = 300; a.block_mask = ctypes.pointer(b)
+    assert _status(a) == fa.FA_ERR_SHAPE  # document masks need Sq == Skv
+
+
+def test_decode_validation_and_workspace_size():
+    a = _args(B=2, Hq=8, Hkv=2, Sq=1, Skv=5000, D=128)
+    n = ctypes.c_size_t()
+    assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    NK = 40
+    bps = 8
+    while bps > 1 and 2 * 2 * -(-NK // bps) < 2048:
+        bps //= 2
+    splits = -(-NK // bps)
+    assert n.value == splits * 2 * 8 * (128 + 1) * 4
+    a = _args(Sq=2)
+    assert _status(a, decode=True) == fa.FA_ERR_SHAPE
+    a = _args(Hq=6, Hkv=2, Sq=1)
+    assert _status(a, decode=True) == fa.FA_ERR_UNSUPPORTED
+    a = _args(Sq=1, Skv=512)
+    assert fa.lib().fa_decode(ctypes.byref(a), None, 0, None) == fa.FA_ERR_WORKSPACE

@@ -1,0 +1,78 @@
+"""Split-KV decode vs the oracle, split-count invariance and decode == forward at Sq = 1."""
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_fa_amd import inputs as gen
+from oracle import flex_oracle as fo
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(q, k, v, lens, score, num_splits=0, Bm=None, extra=None):
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, KV = k.shape[0], k.shape[2]
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    lse = torch.empty((B, q.shape[1], 1), dtype=torch.float32, device="cuda")
+    out = fa.fa_decode(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm,
+                       score=score, num_splits=num_splits, lse=lse)
+    torch.cuda.synchronize()
+    return gen.bf16_bits_to_f32(gen.from_torch_bf16(out)), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("score", ["none", "softcap", "alibi", "bias"])
+def test_decode_matches_oracle(G, D, score):
+    from block_sparse_attention_fa_amd import fa
+    print(f"[case] decode G={G} D={D} score={score}", flush=True)
+    B, Hkv, KV = 3, 2, 1500
+    Hq = G * Hkv
+    q = gen.qkv(40 + G, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(41 + G, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([1500, 700, 129], dtype=np.int32)
+    spec = C.make_spec(42, "kv_len", score, B, Hq, 1, KV, cap=50.0)
+    spec["lens"] = lens
+    got, lse = _decode(q, k, v, lens, C.gpu_score(spec))
+    O, L = fo.decode(q, k, v, lens, C.oracle_score(spec, Hq))
+    C.compare(got, O, f"decode G={G} D={D} {score}")
+    assert np.abs(lse[..., 0] - L[..., 0]).max() < 1e-3 * max(1.0, np.abs(L).max())
+
+
+def test_split_count_invariance_and_forward_equivalence():
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, Hq, Hkv, KV, D = 4, 8, 2, 5000, 128
+    q = gen.qkv(50, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(51, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([5000, 1, 4097, 2500], dtype=np.int32)
+    sc = fa.ScoreMod("softcap", softcap=50.0)
+    outs = [_decode(q, k, v, lens, sc, n)[0] for n in (1, 3, 7, 40, 0)]
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2 ** -7  # one bf16 ulp at |O| < 1 at most
+    O, _ = fo.decode(q, k, v, lens, fo.softcap(50.0))
+    C.compare(outs[0], O, "decode splits")
+    # fa_forward with Sq = 1 and the same BlockMask gives the same answer
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    of = fa.fa_forward(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm, score=sc)
+    torch.cuda.synchronize()
+    C.compare(gen.bf16_bits_to_f32(gen.from_torch_bf16(of)), O, "forward Sq=1")
+
+
+def test_decode_workspace_errors():
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    q = torch.zeros((1, 4, 1, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, 1, 1024, 128), dtype=torch.bfloat16, device="cuda")
+    n = fa.fa_decode_workspace_size(q, kv, kv)
+    assert n > 0
+    small = torch.empty(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_decode(q, kv, kv, workspace=small)
+    assert e.value.status == fa.FA_ERR_WORKSPACE
+    q3 = torch.zeros((1, 3, 1, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_decode(q3, kv, kv)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,155 @@
+"""Forward kernel vs the fp64 oracle, element by element, at sizes that span
+several tiles and a ragged tail, for every mask_mod x score_mod, both head dims,
+GQA, broadcast and per-batch BlockMasks, the superset list encoding and the
+dense path.  Tolerance: max abs 2e-2 and mean abs 2e-3 (bf16 in, fp32 accumulate).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_fa_amd import inputs as gen
+from oracle import flex_oracle as fo
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+
+BATCH_DEP = ("document", "document_causal", "kv_len")
+
+
+def run_case(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense=False,
+             per_head_mask=False, with_lse=True, **spec_kw):
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    print(f"[case] seed={seed} mask={mask} score={score} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} "
+          f"sep={separate_full} dense={dense}", flush=True)
+    q, k, v = gen.qkv(seed, B, Hq, Hkv, Sq, Skv, D)
+    spec = C.make_spec(seed, mask, score, B, Hq, Sq, Skv, **spec_kw)
+    qt, kt, vt = (gen.to_torch_bf16(x) for x in (q, k, v))
+    bm = None
+    if not dense:
+        Bm = B if mask in BATCH_DEP else 1
+        Hm = Hq if per_head_mask else 1
+        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda") if with_lse else None
+    out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=C.gpu_score(spec), lse=lse)
+    torch.cuda.synchronize()
+    got = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    O, L = fo.attention(q, k, v, None if dense else C.oracle_mask(spec), C.oracle_score(spec, Hq))
+    C.compare(got, O, f"{mask}/{score}")
+    if with_lse:
+        gl = lse.cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(np.isneginf(gl), np.isneginf(L))
+        fin = np.isfinite(L)
+        if fin.any():
+            assert np.abs(gl[fin] - L[fin]).max() < 1e-3 * max(1.0, np.abs(L[fin]).max())
+    return got, O
+
+
+def test_tiny_causal_workload():
+    # B=1, H=2, S=256, D=64, causal, no score_mod (2x2 tiles)
+    run_case(1, "causal", "none", 1, 2, 2, 256, 256, 64)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("score", C.SCORE_NAMES)
+@pytest.mark.parametrize("mask", C.MASK_NAMES)
+def test_mask_score_matrix(mask, score, D):
+    run_case(10 + D, mask, score, 2, 4, 2, 300, 300, D)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (1, 257), (129, 129), (640, 640)])
+@pytest.mark.parametrize("mask", ["causal", "sliding_causal", "prefix_lm", "kv_len", "none"])
+def test_uneven_lengths(mask, Sq, Skv):
+    run_case(20, mask, "alibi", 1, 2, 1, Sq, Skv, 128)
+
+
+@pytest.mark.parametrize("mask", ["causal", "document_causal", "sliding_causal"])
+def test_superset_encoding(mask):
+    run_case(30, mask, "softcap", 2, 2, 2, 384, 384, 64, separate_full=False)
+
+
+@pytest.mark.parametrize("score", ["none", "alibi", "bias"])
+def test_dense_without_blockmask(score):
+    run_case(31, "none", score, 1, 4, 4, 250, 250, 128, dense=True)
+
+
+def test_per_head_blockmask_and_gqa8():
+    run_case(32, "causal", "rel_pos", 1, 8, 1, 260, 260, 128, per_head_mask=True)
+
+
+def test_explicit_alibi_slopes_and_broadcast_bias():
+    run_case(33, "causal", "alibi", 2, 4, 2, 270, 270, 64, explicit_slopes=True)
+    run_case(34, "causal", "bias", 2, 4, 2, 270, 270, 64, bias_broadcast=True)
+
+
+def test_fully_masked_rows_are_zero_with_neg_inf_lse():
+    # kv_len = 0 for a batch row: every row of it is empty
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, H, S, D = 2, 2, 200, 64
+    q, k, v = gen.qkv(35, B, H, H, S, S, D)
+    lens = np.array([0, 150], dtype=np.int32)
+    spec = {"mask": "kv_len", "lens": lens, "score": "none"}
+    bm = fa.fa_build_block_mask(C.gpu_mask(spec), B, 1, S, S)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    out = fa.fa_forward(*(gen.to_torch_bf16(x) for x in (q, k, v)), block_mask=bm, lse=lse)
+    torch.cuda.synchronize()
+    o = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0].cpu().numpy()))
+    O, _ = fo.attention(q, k, v, fo.kv_length(lens))
+    C.compare(o, O, "kv_len rows")
+
+
+def test_closed_forms_on_gpu():
+    # uniform V -> constant output; causal row 0 -> V[0]; window 0 -> V
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, H, S, D = 1, 2, 384, 128
+    q, k, v = gen.qkv(36, B, H, H, S, S, D)
+    c = gen.f32_to_bf16_bits(np.linspace(-1, 1, D).astype(np.float32))
+    vu = np.broadcast_to(c, v.shape).copy()
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, 1, S, S)
+    out = fa.fa_forward(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(vu), block_mask=bm,
+                        score=fa.ScoreMod("alibi"))
+    o = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    assert np.abs(o - gen.bf16_bits_to_f32(c)).max() <= 2 ** -7
+    out = fa.fa_forward(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm)
+    o = gen.from_torch_bf16(out)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    bm0 = fa.fa_build_block_mask(fa.MaskMod("sliding_causal", window=0), 1, 1, S, S)
+    out = fa.fa_forward(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gen.from_torch_bf16(out), v)
+
+
+def test_deterministic_repeat():
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, H, S, D = 1, 4, 1024, 128
+    q, k, v = (gen.to_torch_bf16(x) for x in gen.qkv(37, B, H, H, S, S, D))
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, 1, S, S)
+    o1 = fa.fa_forward(q, k, v, block_mask=bm, score=fa.ScoreMod("softcap", softcap=30.0))
+    o2 = fa.fa_forward(q, k, v, block_mask=bm, score=fa.ScoreMod("softcap", softcap=30.0))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_invalid_arguments_raise():
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    q = torch.zeros((1, 3, 128, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 128, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_forward(q, k, k)
+    assert e.value.status == fa.FA_ERR_SHAPE
+    q = torch.zeros((1, 2, 128, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_forward(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, 1, 256, 256)
+    q = torch.zeros((1, 2, 200, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_forward(q, q, q, block_mask=bm)  # built for other lengths
+    assert e.value.status == fa.FA_ERR_SHAPE
