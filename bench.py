@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse FlexAttention hot path on one MI355X.
+
+One step = fa_build_block_mask + fa_forward on the causal + ALiBi workload
+(B=4, H=16, S=8192, D=128, bf16 ~N(0,1); slopes 2^(-8(h+1)/16)); the reported
+value is attended TFLOP/s (4*D per attended (b,h,q,kv) position).  The
+split-KV decode (B=32, Hq=32, Hkv=8, D=128, KV cache 32768 with valid lengths
+uniform in [4096, 32768], softcap 50) is timed in the same run and reported as
+HBM GB/s.  Inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+FWD = dict(name="causal+alibi fwd B4 H16 S8192 D128 bf16", workload_id=2, B=4, H=16, S=8192, D=128)
+DEC = dict(name="gqa4 split-kv decode B32 Hq32 Hkv8 D128 KV32768 softcap50 bf16", workload_id=5,
+           B=32, Hq=32, Hkv=8, D=128, KV=32768, len_lo=4096, len_hi=32768, cap=50.0)
+
+FWD_SOURCES = ["fwd_kernel.hpp", "mods.hpp", "fwd_causal.hip", "fa_internal.hpp"]
+DEC_SOURCES = ["decode.hip", "mods.hpp", "fa_internal.hpp"]
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_sparse_attention_fa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(summary, files):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"source_sha:\s*(\w+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b or m_sha.group(1) != source_sha(files):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(q, k, v, seconds):
+    """The fp64 oracle on host cores, on (b, h, 1024-row) chunks of the forward
+    workload taken from the last rows backwards until `seconds` have elapsed."""
+    import numpy as np
+    from oracle import flex_oracle as fo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+    mask, score = fo.causal(), fo.alibi(fo.default_alibi_slopes(H))
+    chunks, flops = [], 0.0
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(H):
+            for r1 in range(S, 0, -1024):
+                rows = np.arange(max(0, r1 - 1024), r1)
+                fo.attention_rows(q, k, v, b, h, rows, mask, score)
+                flops += 4.0 * D * float((rows + 1).sum())  # causal: row q attends q+1 keys
+                chunks.append((b, h, int(rows[0])))
+                if time.perf_counter() - t0 >= seconds:
+                    break
+            else:
+                continue
+            break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(chunks)} chunks of 1024 query rows x all 8192 keys (fp64, dense) of the "
+                      f"causal+ALiBi S=8192 workload, (b,h) in order from (0,0), rows from the end back; {dt:.1f} s; "
+                      f"host cpu_count={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this build has no multi-GPU path "
+                  "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    from block_sparse_attention_fa_amd import inputs as gen
+
+    fa.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+
+    # ---------------- forward workload ----------------
+    B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+    print(f"[bench] generating {FWD['name']}", file=sys.stderr, flush=True)
+    q, k, v = gen.qkv(FWD["workload_id"], B, H, H, S, S, D)
+    qt, kt, vt = (gen.to_torch_bf16(x, dev) for x in (q, k, v))
+    out = torch.empty_like(qt)
+    mask, score = fa.MaskMod("causal"), fa.ScoreMod("alibi")
+    bm = fa.BlockMask(mask, 1, 1, S, S, device=dev)
+    stream = torch.cuda.current_stream()
+    L = fa.lib()
+    import ctypes
+    args_c = fa._attn_args(qt, kt, vt, out, None, bm, score, 0.0, 0)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(ev=None):
+        fa._check(L.fa_build_block_mask(ctypes.byref(bm.c), S, S, sptr))
+        if ev is not None:
+            ev[0].record(stream)
+        fa._check(L.fa_forward(ctypes.byref(args_c), sptr))
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    # block mask build alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        fa._check(L.fa_build_block_mask(ctypes.byref(bm.c), S, S, sptr))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1) / 10
+    cls = bm.classes()
+    n_part, n_full = int((cls == 1).sum()), int((cls == 2).sum())
+
+    n_att = B * H * S * (S + 1) // 2               # causal: row q attends q+1 keys
+    att_flops = 4.0 * D * n_att
+    exec_flops = 4.0 * D * 128 * 128 * (n_part + n_full) * B * H
+    alg_bytes = 4 * B * H * S * D * 2               # Q, K, V, O once each
+    fwd_tflops = att_flops / (fwd_ms * 1e-3) / 1e12
+    value = att_flops / (step_ms * 1e-3) / 1e12
+    traffic = read_traffic("fwd_causal_alibi_8192_traffic.md", FWD_SOURCES)
+
+    result = {
+        "metric": "fwd attended TFLOP/s & % bf16 MFMA peak; decode HBM GB/s (1 MI355X)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": FWD["name"], "B": B, "H": H, "S": S, "D": D, "mask": "causal",
+                   "score_mod": "alibi", "block": 128, "step": "fa_build_block_mask + fa_forward"},
+        "fwd": {"kernel_ms": round(fwd_ms, 4), "attended_tflops": round(fwd_tflops, 2),
+                "frac_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                "executed_tile_tflops": round(exec_flops / (fwd_ms * 1e-3) / 1e12, 2),
+                "tiles_partial": n_part, "tiles_full": n_full, "blockmask_build_ms": round(build_ms, 4),
+                "sparsity_pct": round(100.0 * float((cls == 0).sum()) / cls.size, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "kernel": "fwd_kernel<128, MaskCausal, ScoreAlibi>"},
+    }
+    del qt, kt, vt, out
+    torch.cuda.empty_cache()
+
+    # ---------------- decode workload ----------------
+    if not args.no_decode:
+        Bd, Hq, Hkv, Dd, KV = DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["D"], DEC["KV"]
+        print(f"[bench] generating {DEC['name']}", file=sys.stderr, flush=True)
+        qd = gen.qkv(DEC["workload_id"], Bd, Hq, Hkv, 1, 1, Dd)[0]
+        _, kc, vc = gen.qkv(DEC["workload_id"] + 100, Bd, Hkv, Hkv, 1, KV, Dd)
+        lens = gen.kv_lengths(DEC["workload_id"], Bd, DEC["len_lo"], DEC["len_hi"])
+        qdt = gen.to_torch_bf16(qd, dev)
+        kct = gen.to_torch_bf16(kc, dev)
+        del kc
+        vct = gen.to_torch_bf16(vc, dev)
+        del vc
+        lens_t = torch.from_numpy(lens).to(dev)
+        bmd = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=lens_t), Bd, 1, 1, KV, device=dev)
+        od = torch.empty_like(qdt)
+        sc = fa.ScoreMod("softcap", softcap=DEC["cap"])
+        ws = torch.empty(fa.fa_decode_workspace_size(qdt, kct, vct, bmd, sc) // 4 + 1,
+                         dtype=torch.float32, device=dev)
+        for _ in range(3):
+            fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.decode_steps):
+            fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.decode_steps
+        kv_bytes = int(lens.astype(np.int64).sum()) * Hkv * Dd * 2 * 2
+        dec_bytes = kv_bytes + 2 * Bd * Hq * Dd * 2
+        gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": DEC["name"], "ms": round(dec_ms, 4), "GB/s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": read_traffic("decode_gqa4_kv32768_traffic.md", DEC_SOURCES),
+                         "kernels": "decode_partial_kernel<128,4,ScoreSoftcap> + decode_merge_kernel<128>"}}
+        del qdt, kct, vct
+        torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline (oracle) ----------------
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,23 +8,30 @@
 // (§4.3).
 //
 // Work decomposition: one 256-thread workgroup (4 waves) per (b, hq, 128-row
-// query tile).  Wave w owns query rows 32w..32w+31 of the tile.
+// query tile); wave w owns query rows 32w..32w+31.  Two workgroups share a CU
+// (<= 256 registers per lane, 64 KiB of LDS each), so one workgroup's matrix
+// work overlaps the other's softmax, loads and barriers.
 //
 // MFMA orientation.  Both products are computed transposed so that every
 // lane owns exactly one query row (lane % 32) in both accumulators:
 //   S^T[kv, q] = K[kv, :] . Q[q, :]      (A = K tile from LDS, B = Q^T in registers)
-//   O^T[d, q] += V^T[d, kv] . P^T[kv, q] (A = V^T tile from LDS, B = P^T in registers)
+//   O^T[d, q] += V^T[d, kv] . P^T[kv, q] (A = V^T read transposed from LDS, B = P^T)
 // with v_mfma_f32_32x32x16_bf16.  In a 32x32 accumulator lane l holds column
-// l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  So the row max and
-// row sum of the softmax reduce over the lane's own 64 values and then one
-// swap with lane l ^ 32, the O rescale is a per-lane scalar, and the P
-// values come out of the S accumulator already in the B-operand layout of
-// the PV product (the k index is a permutation of the 16 keys of each step,
-// which V^T in LDS is stored to match).
+// l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  So the softmax row
+// max and row sum reduce over the lane's own 64 values plus one swap with
+// lane l ^ 32, the O rescale is a per-lane scalar, and the P values leave the
+// S accumulator already laid out as the B operand of the PV product: the 16
+// keys of a PV k-step sit in lane half h at kv = 4h + {0..3} and 8 + 4h + {0..3}.
+// The matching V^T operand comes from row-major V in LDS through
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
+// of the 8-byte row pointed to by lane 4j + i/4 (j = 0..3), so lanes pointing
+// at a 4-key x 16-dim block of V receive one dim each across the 4 keys.
 //
-// LDS: the K tile row-major [128][D+8] and V transposed [D][128+8] (both
-// padded by 16 bytes per row against bank conflicts).  The next tile's K/V
-// rows are loaded into registers while the current tile is computed.
+// Data movement: K and V tiles go from global memory straight into LDS with
+// 16-byte global_load_lds (no registers), row-major with the 16-byte chunks
+// of row r XOR-swizzled by r (bank-conflict-free column reads).  The K tile
+// of step t+1 streams in during the softmax and PV of step t; the V tile of
+// step t+1 during QK^T and softmax of step t+1.
 #pragma once
 
 #include <type_traits>
@@ -34,20 +41,19 @@
 namespace fa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kFwdThreads = 256;
 constexpr int kBM = FA_BLOCK;  // query rows per workgroup
 constexpr int kBN = FA_BLOCK;  // keys per tile
-
-template <int D>
-struct FwdSmem {
-  static constexpr int KSTR = D + 8;    // elements per K row
-  static constexpr int VSTR = kBN + 8;  // elements per V^T row
-  uint16_t k[kBN * KSTR];
-  uint16_t vt[D * VSTR];
-};
+// Lazy rescaling: the running max used for the exponentials is only raised
+// when a tile's max exceeds it by more than this (base-2 units), so the
+// exponentials stay <= 2^8 and the O rescale is skipped for most tiles.
+constexpr float kRescaleSlack = 8.0f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give each
 // XCD a contiguous range of logical tile ids, so the query tiles of one head
@@ -58,26 +64,45 @@ __device__ __forceinline__ int xcd_logical_id(int bid, int total) {
   return x * per + min(x, rem) + j;
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo16, b.lo16)
+// Waits until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order, so everything older than the N newest is done).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi16, b.hi16)
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_address(const void* ptr) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ptr;
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (global_load_lds_dwordx4).
+// Written as asm so that the compiler does not insert its own conservative
+// vmcnt(0) waits before every LDS read; the kernels wait explicitly instead.
+// No register is written by the load, only LDS.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gaddr), "s"(lds) : "memory");
 }
 
 template <int D, class Mask, class Score>
-__global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
-  constexpr int KS = D / 16;        // k-steps of the QK^T product
-  constexpr int DT = D / 32;        // 32-row blocks of O^T
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int KCH = kBN * CPR / kFwdThreads;  // K chunks staged per thread
-  constexpr int VTHREADS = 2 * D;   // threads that stage V (8 rows x 8 d each)
-  using Smem = FwdSmem<D>;
-  __shared__ __align__(16) Smem sm;
+  constexpr int KS = D / 16;                  // k-steps of the QK^T product
+  constexpr int DT = D / 32;                  // 32-row blocks of O^T
+  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int HB = 64;                      // keys per sub-tile (half a BlockMask tile)
+  constexpr int NI = HB * CPR / 64 / 4;       // 16-byte loads per wave per sub-tile buffer
+  // two stages of K and V sub-tiles, row-major, chunks XOR-swizzled by row
+  __shared__ __align__(16) uint16_t k_lds[2][HB * D];
+  __shared__ __align__(16) uint16_t v_lds[2][HB * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lq = lane & 31, hh = lane >> 5;
 
   // ---- which (b, hq, query tile) ------------------------------------------
@@ -112,11 +137,45 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
     }
   }
   const int T = n_part + n_full;
+  auto kb_of = [&](int t) -> int {
+    if (t < n_part) return part_idx[t];
+    return bm.dense ? (t - n_part) : full_idx[t - n_part];
+  };
 
   const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1];
   const uint16_t* Kp = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1];
   const uint16_t* Vp = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1];
   const long long ks2 = p.ks[2], vs2 = p.vs[2];
+
+  // ---- global -> LDS sub-tile loads -------------------------------------------
+  // Sub-tile j = keys [64 (j % 2), 64 (j % 2) + 64) of BlockMask tile kb_of(j / 2).
+  // LDS slot s (16 bytes) holds row s / CPR, chunk (s % CPR) ^ (row % CPR); wave w
+  // issues slots [64 (4i + w), +64) for i < NI.  Rows past Skv re-read row Skv-1
+  // (finite values whose scores are masked to -inf).
+  // Within one instruction the 64 lanes cover 64 / CPR consecutive rows; the
+  // swizzled chunk of a lane does not depend on i, so a per-lane offset plus a
+  // uniform row step per instruction addresses every load.
+  constexpr int RPI = 64 / CPR;                                  // rows per instruction
+  const int lrow = wave * RPI + lane / CPR;                      // row of this lane in instruction 0
+  const int lchunk = (lane % CPR) ^ (lrow % CPR);                // its logical chunk
+  auto issue = [&](const uint16_t* g, long long rs, const uint16_t* buf, int j) {
+    const int kv0 = kb_of(j >> 1) * kBN + HB * (j & 1);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf)) + 16 * 64 * wave;
+    if (kv0 + HB <= p.Skv) {
+      const uint16_t* gl = g + (long long)(kv0 + lrow) * rs + 8 * lchunk;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(gl + (long long)(4 * RPI * i) * rs, base + 16 * 64 * 4 * i);
+    } else {
+      const int last = p.Skv - 1 - kv0;  // rows past Skv re-read row Skv-1
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rr = min(lrow + 4 * RPI * i, last);
+        dma16(g + (long long)(kv0 + rr) * rs + 8 * lchunk, base + 16 * 64 * 4 * i);
+      }
+    }
+  };
+  auto lds_off = [](int r, int chunk) { return r * D + (((chunk ^ r) % CPR) * 8); };
 
   // ---- per-lane query row ---------------------------------------------------
   const int myq = q0 + wave * 32 + lq;
@@ -132,88 +191,30 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
   const auto mrow = Mask::row(p.mask, b, hq, qc);
   const auto srow = Score::row(p.score, b, hq, qc);
 
-  // ---- staging of K/V tiles through registers -------------------------------
-  u32x4_t kreg[KCH];
-  u32x4_t vreg[8];
-  const int vc = tid % CPR;                 // d chunk this thread stages for V
-  const int vhalf = (tid / CPR) & 1;
-  const int vg = tid / (2 * CPR);           // 16-key group
-  auto kb_of = [&](int t) -> int {
-    if (t < n_part) return part_idx[t];
-    return bm.dense ? (t - n_part) : full_idx[t - n_part];
-  };
-  auto load_tile = [&](int kb) {
-    const int kv0 = kb * kBN;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + kFwdThreads * i;
-      const int r = ci / CPR, c = ci % CPR;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (kv0 + r < p.Skv) x = *(const u32x4_t*)(Kp + (long long)(kv0 + r) * ks2 + 8 * c);
-      kreg[i] = x;
-    }
-    if (tid < VTHREADS) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 16 * vg + 4 * vhalf + (j & 3) + 8 * (j >> 2);
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (kv0 + r < p.Skv) x = *(const u32x4_t*)(Vp + (long long)(kv0 + r) * vs2 + 8 * vc);
-        vreg[j] = x;
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + kFwdThreads * i;
-      const int r = ci / CPR, c = ci % CPR;
-      *(u32x4_t*)&sm.k[r * Smem::KSTR + 8 * c] = kreg[i];
-    }
-    if (tid < VTHREADS) {
-      // 8 keys x 8 dims -> 8 dims x 8 keys.  The keys of this thread are, in
-      // order, 16g + 4*half + {0..3} and 16g + 8 + 4*half + {0..3}; they land at
-      // positions 16g + 8*half + {0..7} of each V^T row, the order in which
-      // the P^T operand lists its keys.
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int w = dd >> 1;
-        u32x4_t o;
-        if (dd & 1) {
-          o[0] = pack_hi(vreg[0][w], vreg[1][w]);
-          o[1] = pack_hi(vreg[2][w], vreg[3][w]);
-          o[2] = pack_hi(vreg[4][w], vreg[5][w]);
-          o[3] = pack_hi(vreg[6][w], vreg[7][w]);
-        } else {
-          o[0] = pack_lo(vreg[0][w], vreg[1][w]);
-          o[1] = pack_lo(vreg[2][w], vreg[3][w]);
-          o[2] = pack_lo(vreg[4][w], vreg[5][w]);
-          o[3] = pack_lo(vreg[6][w], vreg[7][w]);
-        }
-        *(u32x4_t*)&sm.vt[(8 * vc + dd) * Smem::VSTR + 16 * vg + 8 * vhalf] = o;
-      }
-    }
-  };
-
   // ---- online softmax state (base-2 units) ----------------------------------
   f32x16_t oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16_t{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;  // this lane's half of the row sum
+  float m_run = -INFINITY;  // max the exponentials are taken against
+  float l_run = 0.0f;       // this lane's half of the row sum
 
-  auto compute_tile = [&](int kb, auto partial_tag) {
+  auto compute_subtile = [&](int j, int kb, auto partial_tag) {
     constexpr bool kPartialTile = decltype(partial_tag)::value;
-    const int kvt0 = kb * kBN;
-    const bool ragged = kvt0 + kBN > p.Skv;
+    const int buf = j & 1;
+    const int kvt0 = kb * kBN + HB * (j & 1);
+    const bool ragged = kvt0 + HB > p.Skv;
+    const uint16_t* kl = k_lds[buf];
+    const uint16_t* vl = v_lds[buf];
 
-    // S^T = K Q^T
-    f32x16_t sacc[4];
+    // S^T = K Q^T  (2 blocks of 32 keys)
+    f32x16_t sacc[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
       sacc[mt] = f32x16_t{};
+      const int r = 32 * mt + lq;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t a = *(const bf16x8_t*)&sm.k[(32 * mt + lq) * Smem::KSTR + 16 * s + 8 * hh];
+        const bf16x8_t a = *(const bf16x8_t*)&kl[lds_off(r, 2 * s + hh)];
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[mt], 0, 0, 0);
       }
     }
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
     // score_mod, mask_mod (partial tiles only), out-of-range keys
     float mloc = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kv = kvt0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -234,15 +235,20 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
       }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    if (__any(mloc > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
     float lsum = 0.0f;
-    bf16x8_t pb[4][2];
+    bf16x8_t pb[2][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = __builtin_amdgcn_exp2f(sacc[mt][r] - m_use);
@@ -250,36 +256,55 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
         pb[mt][r >> 3][r & 7] = (__bf16)e;
       }
     }
-    l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+    l_run += lsum;
 
     // O^T += V^T P^T
+    const int gi = lane >> 4, si = lane & 15;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int s = 0; s < 2; ++s) {
+        const int row0 = 32 * mt + 16 * s + 4 * hh + (si >> 2);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_t a =
-              *(const bf16x8_t*)&sm.vt[(32 * dt + lq) * Smem::VSTR + 16 * (2 * mt + s) + 8 * hh];
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
+          const int off_lo = lds_off(row0, d >> 3) + (d & 7);
+          const int off_hi = lds_off(row0 + 8, d >> 3) + (d & 7);
+          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_lo));
+          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_hi));
+          const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mt][s], oacc[dt], 0, 0, 0);
         }
       }
     }
   };
 
-  if (T > 0) load_tile(kb_of(0));
-  for (int t = 0; t < T; ++t) {
-    const int kb = kb_of(t);
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < T) load_tile(kb_of(t + 1));
-    if (t < n_part)
-      compute_tile(kb, std::true_type{});
-    else
-      compute_tile(kb, std::false_type{});
+  const int J = 2 * T;
+  if (J > 0) {
+    issue(Kp, ks2, k_lds[0], 0);
+    issue(Vp, vs2, v_lds[0], 0);
+    issue(Kp, ks2, k_lds[1], 1);
+    issue(Vp, vs2, v_lds[1], 1);
+    for (int j = 0; j < J; ++j) {
+      // K(j), V(j) landed for every wave; K(j+1), V(j+1) may still be in flight
+      if (j + 1 < J)
+        wait_vmcnt<2 * NI>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      const int t = j >> 1;
+      if (t < n_part)
+        compute_subtile(j, kb_of(t), std::true_type{});
+      else
+        compute_subtile(j, kb_of(t), std::false_type{});
+      // every wave is done reading stage j % 2: refill it with sub-tile j + 2
+      wait_lds_reads();
+      __builtin_amdgcn_s_barrier();
+      if (j + 2 < J) {
+        issue(Kp, ks2, k_lds[j & 1], j + 2);
+        issue(Vp, vs2, v_lds[j & 1], j + 2);
+      }
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -292,7 +317,6 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dt + 8 * g + 4 * hh;
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         bf16x4_t o4;
         o4[0] = (__bf16)(oacc[dt][4 * g + 0] * inv);
         o4[1] = (__bf16)(oacc[dt][4 * g + 1] * inv);

@@ -47,17 +47,30 @@ def _normal_bf16(seed, shape, std=1.0) -> np.ndarray:
     return f32_to_bf16_bits(x).reshape(shape)
 
 
+def _normal_bf16_per_head(seed, shape, threads=8) -> np.ndarray:
+    """[B,H,S,D] ~N(0,1) bf16 bits; slice (b,h) comes from generator seed + [b, h]."""
+    B, H = shape[0], shape[1]
+    out = np.empty(shape, dtype=np.uint16)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = _normal_bf16(list(seed) + [b, h], shape[2:])
+
+    if threads > 1 and B * H > 1 and int(np.prod(shape)) >= (1 << 22):
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(B * H)))
+    else:
+        for bh in range(B * H):
+            fill(bh)
+    return out
+
+
 def qkv(workload_id: int, B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D: int):
-    """Q [B,Hq,Sq,D], K and V [B,Hkv,Skv,D] as bf16 bits, ~N(0,1)."""
-    q = _normal_bf16([workload_id, STREAM_Q], (B, Hq, Sq, D))
-    k = _normal_bf16([workload_id, STREAM_K], (B, Hkv, Skv, D))
-    v = _normal_bf16([workload_id, STREAM_V], (B, Hkv, Skv, D))
+    """Q [B,Hq,Sq,D], K and V [B,Hkv,Skv,D] as bf16 bits, ~N(0,1), one generator per (b, h)."""
+    q = _normal_bf16_per_head([workload_id, STREAM_Q], (B, Hq, Sq, D))
+    k = _normal_bf16_per_head([workload_id, STREAM_K], (B, Hkv, Skv, D))
+    v = _normal_bf16_per_head([workload_id, STREAM_V], (B, Hkv, Skv, D))
     return q, k, v
-
-
-def one_tensor(workload_id: int, stream: int, shape) -> np.ndarray:
-    """A single ~N(0,1) bf16 tensor from the given stream (used for large KV caches)."""
-    return _normal_bf16([workload_id, stream], tuple(shape))
 
 
 def document_ids(workload_id: int, B: int, S: int, lo: int = 256, hi: int = 4096) -> np.ndarray:
