@@ -29,7 +29,7 @@
 //
 // Data movement: K and V tiles go from global memory straight into LDS with
 // 16-byte global_load_lds (no registers), row-major with the 16-byte chunks
-// of row r XOR-swizzled by r (bank-conflict-free column reads).  The K tile
+// of each row XOR-swizzled (bank-conflict-free reads, see k_swizzle/v_swizzle).  The K tile
 // of step t+1 streams in during the softmax and PV of step t; the V tile of
 // step t+1 during QK^T and softmax of step t+1.
 #pragma once
@@ -81,10 +81,45 @@ __device__ __forceinline__ uint32_t lds_address(const void* ptr) {
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane (global_load_lds_dwordx4).
 // Written as asm so that the compiler does not insert its own conservative
 // vmcnt(0) waits before every LDS read; the kernels wait explicitly instead.
-// No register is written by the load, only LDS.
+// No register is written by the load, only LDS.  No "memory" clobber (it
+// would stop the block-list reads from being scalar loads): ordering against
+// LDS reads comes from the volatile wait/barrier statements around it, which
+// do clobber memory and which volatile asm cannot be reordered with.
+// dma16: 64-bit per-lane address.  dma16s: uniform 64-bit base + 32-bit
+// per-lane byte offset (one VGPR per lane).
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(lds) : "memory");
+               :: "v"(gaddr), "s"(lds));
+}
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds));
+}
+
+// A pointer the compiler can keep in SGPRs (the value is the same in every lane).
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t v = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// LDS swizzles (16-byte chunk index XOR a function of the row), chosen per
+// read pattern so that each group of lanes served together touches distinct
+// banks (64 banks of 4 bytes: a 256-byte window):
+//  * K, read with ds_read_b128 by 16 lanes = 16 consecutive rows, one chunk:
+//    D=128 (one row per window) XOR row % 16; D=64 (two rows per window)
+//    XOR (row / 2) % 8.
+//  * V, read with ds_read_b64_tr_b16 by 16 lanes = 4 consecutive rows x two
+//    adjacent chunks (and by the wave: 8 rows x 4 chunks):
+//    D=128 XOR 4 (row % 4); D=64 XOR 4 ((row / 2) % 2).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
 template <int D, class Mask, class Score>
@@ -149,23 +184,26 @@ void fwd_kernel(FwdParams p) {
 
   // ---- global -> LDS sub-tile loads -------------------------------------------
   // Sub-tile j = keys [64 (j % 2), 64 (j % 2) + 64) of BlockMask tile kb_of(j / 2).
-  // LDS slot s (16 bytes) holds row s / CPR, chunk (s % CPR) ^ (row % CPR); wave w
-  // issues slots [64 (4i + w), +64) for i < NI.  Rows past Skv re-read row Skv-1
-  // (finite values whose scores are masked to -inf).
+  // LDS slot s (16 bytes) holds row s / CPR, logical chunk (s % CPR) ^ swizzle(row);
+  // wave w issues slots [64 (4i + w), +64) for i < NI.  Rows past Skv re-read
+  // row Skv-1 (finite values whose scores are masked to -inf).
   // Within one instruction the 64 lanes cover 64 / CPR consecutive rows; the
-  // swizzled chunk of a lane does not depend on i, so a per-lane offset plus a
-  // uniform row step per instruction addresses every load.
+  // swizzled chunk of a lane does not depend on i (the swizzles only use row
+  // bits below 4 * RPI), so a per-lane offset plus a uniform row step per
+  // instruction addresses every load.
   constexpr int RPI = 64 / CPR;                                  // rows per instruction
   const int lrow = wave * RPI + lane / CPR;                      // row of this lane in instruction 0
-  const int lchunk = (lane % CPR) ^ (lrow % CPR);                // its logical chunk
-  auto issue = [&](const uint16_t* g, long long rs, const uint16_t* buf, int j) {
+  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);          // logical chunks it loads
+  const int vchunk = (lane % CPR) ^ v_swizzle<D>(lrow);
+  const uint32_t k_voff = (uint32_t)(2 * lrow * ks2 + 16 * kchunk);  // bytes
+  const uint32_t v_voff = (uint32_t)(2 * lrow * vs2 + 16 * vchunk);
+  auto issue = [&](const uint16_t* g, long long rs, const uint16_t* buf, int lchunk, uint32_t voff, int j) {
     const int kv0 = kb_of(j >> 1) * kBN + HB * (j & 1);
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf)) + 16 * 64 * wave;
     if (kv0 + HB <= p.Skv) {
-      const uint16_t* gl = g + (long long)(kv0 + lrow) * rs + 8 * lchunk;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        dma16(gl + (long long)(4 * RPI * i) * rs, base + 16 * 64 * 4 * i);
+        dma16s(voff, uniform_ptr(g + (long long)(kv0 + 4 * RPI * i) * rs), base + 16 * 64 * 4 * i);
     } else {
       const int last = p.Skv - 1 - kv0;  // rows past Skv re-read row Skv-1
 #pragma unroll
@@ -175,7 +213,9 @@ void fwd_kernel(FwdParams p) {
       }
     }
   };
-  auto lds_off = [](int r, int chunk) { return r * D + (((chunk ^ r) % CPR) * 8); };
+  // element offsets of (row, logical chunk) in the K and V stages
+  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
+  auto v_off = [](int r, int chunk) { return r * D + ((chunk ^ v_swizzle<D>(r)) * 8); };
 
   // ---- per-lane query row ---------------------------------------------------
   const int myq = q0 + wave * 32 + lq;
@@ -195,11 +235,15 @@ void fwd_kernel(FwdParams p) {
   f32x16_t oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x16_t{};
-  float m_run = -INFINITY;  // max the exponentials are taken against
+  // Reference max of the exponentials: -inf until the row sees a finite score,
+  // then only raised when a score exceeds it by more than kRescaleSlack.  Scores
+  // are produced relative to it (y = x2 - m_run), so exp2(y) needs no subtraction.
+  float m_run = -INFINITY;
   float l_run = 0.0f;       // this lane's half of the row sum
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute_subtile = [&](int j, int kb, auto partial_tag) {
-    constexpr bool kPartialTile = decltype(partial_tag)::value;
+  auto compute_subtile = [&](int j, int kb, bool partial) {
     const int buf = j & 1;
     const int kvt0 = kb * kBN + HB * (j & 1);
     const bool ragged = kvt0 + HB > p.Skv;
@@ -214,49 +258,77 @@ void fwd_kernel(FwdParams p) {
       const int r = 32 * mt + lq;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8_t a = *(const bf16x8_t*)&kl[lds_off(r, 2 * s + hh)];
+        const bf16x8_t a = *(const bf16x8_t*)&kl[k_off(r, 2 * s + hh)];
         sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[mt], 0, 0, 0);
       }
     }
 
-    // score_mod, mask_mod (partial tiles only), out-of-range keys
-    float mloc = -INFINITY;
+    // Element (mt, r) of this lane holds key kvb + cr, cr = 32 mt + 8 (r/4) + r%4.
+    // score_mod everywhere; mask_mod on partial tiles; keys past Skv on the ragged tile.
+    const int kvb = kvt0 + 4 * hh;
+    const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
+    const auto st = Score::tile(srow, kvb, m_ref);
+    float ymax = -INFINITY;
+    if (!partial && !ragged) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kv = kvt0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        bool keep = true;
-        if (ragged) keep = kv < p.Skv;
-        if constexpr (kPartialTile) keep = keep && mrow(kv);
-        const float x = keep ? Score::apply1(srow, sacc[mt][r], kv, 0) : -INFINITY;
-        sacc[mt][r] = x;
-        mloc = fmaxf(mloc, x);
+        for (int r = 0; r < 16; ++r) {
+          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+          const float y = Score::apply(st, sacc[mt][r], cr);
+          sacc[mt][r] = y;
+          ymax = fmaxf(ymax, y);
+        }
+      }
+    } else {
+      const auto mtl = Mask::tile(mrow, kvb);
+      const int lim = ragged ? p.Skv - kvb : HB;  // key kvb + cr exists iff cr < lim
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+          const int crs = min(cr, lim - 1);  // in-bounds index for functors that load
+          bool keep = cr < lim;
+          if (partial) keep = keep && Mask::keep(mtl, crs);
+          const float y = keep ? Score::apply(st, sacc[mt][r], crs) : -INFINITY;
+          sacc[mt][r] = y;
+          ymax = fmaxf(ymax, y);
+        }
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    if (__any(mloc > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    ymax = fmaxf(ymax, __shfl_xor(ymax, 32));
+    const bool raise = ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY);
+    if (__any(raise)) {
+      const float m_new = fmaxf(m_run, m_ref + ymax);
+      const float shift = m_new == -INFINITY ? 0.0f : m_ref - m_new;
+      const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] += shift;
       m_run = m_new;
     }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
-    float lsum = 0.0f;
+    // P = exp2(y) in bf16; the row sum adds the rounded values (v_dot2 with ones)
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(sacc[mt][r] - m_use);
-        lsum += e;
-        pb[mt][r >> 3][r & 7] = (__bf16)e;
+      for (int s = 0; s < 2; ++s) {
+        bf16x2_t pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pk[k][0] = (__bf16)__builtin_amdgcn_exp2f(sacc[mt][8 * s + 2 * k]);
+          pk[k][1] = (__bf16)__builtin_amdgcn_exp2f(sacc[mt][8 * s + 2 * k + 1]);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, l_run, false);
+        }
+        pb[mt][s] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                            __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
-    l_run += lsum;
 
     // O^T += V^T P^T
     const int gi = lane >> 4, si = lane & 15;
@@ -268,8 +340,8 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
-          const int off_lo = lds_off(row0, d >> 3) + (d & 7);
-          const int off_hi = lds_off(row0 + 8, d >> 3) + (d & 7);
+          const int off_lo = v_off(row0, d >> 3) + (d & 7);
+          const int off_hi = v_off(row0 + 8, d >> 3) + (d & 7);
           const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_lo));
           const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_hi));
           const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -281,10 +353,10 @@ void fwd_kernel(FwdParams p) {
 
   const int J = 2 * T;
   if (J > 0) {
-    issue(Kp, ks2, k_lds[0], 0);
-    issue(Vp, vs2, v_lds[0], 0);
-    issue(Kp, ks2, k_lds[1], 1);
-    issue(Vp, vs2, v_lds[1], 1);
+    issue(Kp, ks2, k_lds[0], kchunk, k_voff, 0);
+    issue(Vp, vs2, v_lds[0], vchunk, v_voff, 0);
+    issue(Kp, ks2, k_lds[1], kchunk, k_voff, 1);
+    issue(Vp, vs2, v_lds[1], vchunk, v_voff, 1);
     for (int j = 0; j < J; ++j) {
       // K(j), V(j) landed for every wave; K(j+1), V(j+1) may still be in flight
       if (j + 1 < J)
@@ -293,16 +365,13 @@ void fwd_kernel(FwdParams p) {
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       const int t = j >> 1;
-      if (t < n_part)
-        compute_subtile(j, kb_of(t), std::true_type{});
-      else
-        compute_subtile(j, kb_of(t), std::false_type{});
+      compute_subtile(j, kb_of(t), t < n_part);
       // every wave is done reading stage j % 2: refill it with sub-tile j + 2
       wait_lds_reads();
       __builtin_amdgcn_s_barrier();
       if (j + 2 < J) {
-        issue(Kp, ks2, k_lds[j & 1], j + 2);
-        issue(Vp, vs2, v_lds[j & 1], j + 2);
+        issue(Kp, ks2, k_lds[j & 1], kchunk, k_voff, j + 2);
+        issue(Vp, vs2, v_lds[j & 1], vchunk, v_voff, j + 2);
       }
     }
   }

@@ -11,7 +11,9 @@
 //
 // Every functor is split into a per-query-row part (`row`) evaluated once per
 // lane and a per-key part evaluated per element, because each lane of the
-// kernels owns one query row.
+// kernels owns one query row.  The forward additionally uses a per-tile form:
+// `tile(row, kvb)` folds everything that is constant over a tile, and the
+// per-element call takes the key as kvb + cr with cr a compile-time offset.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +40,9 @@ struct MaskNone {
     __device__ __forceinline__ bool operator()(int) const { return true; }
   };
   static __device__ __forceinline__ Row row(const MaskParams&, int, int, int) { return {}; }
+  struct Tile {};
+  static __device__ __forceinline__ Tile tile(const Row&, int) { return {}; }
+  static __device__ __forceinline__ bool keep(const Tile&, int) { return true; }
 };
 
 // Concepts "mask_mod": causal, q >= kv.
@@ -48,6 +53,11 @@ struct MaskCausal {
     __device__ __forceinline__ bool operator()(int kv) const { return q >= kv; }
   };
   static __device__ __forceinline__ Row row(const MaskParams&, int, int, int q) { return {q}; }
+  struct Tile {
+    int dq;  // q - kvb
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.q - kvb}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr <= t.dq; }
 };
 
 // The window term of Concepts "Composing masks": q - kv <= window.
@@ -60,6 +70,11 @@ struct MaskWindow {
   static __device__ __forceinline__ Row row(const MaskParams& p, int, int, int q) {
     return {q - p.window};
   }
+  struct Tile {
+    int lo;  // q - window - kvb
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.lo - kvb}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr >= t.lo; }
 };
 
 // Talk summary (variant list) / paper review §5.3: same document only.
@@ -74,6 +89,12 @@ struct MaskDocument {
     const int* d = p.doc + (long long)b * p.doc_stride_b;
     return {d, d[q]};
   }
+  struct Tile {
+    const int* doc;  // doc + kvb
+    int dq;
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.doc + kvb, r.dq}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return t.doc[cr] == t.dq; }
 };
 
 // The prefix term of paper review §4.4: keys before prefix_len are visible to all.
@@ -84,6 +105,11 @@ struct MaskPrefix {
     __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
   };
   static __device__ __forceinline__ Row row(const MaskParams& p, int, int, int) { return {p.prefix_len}; }
+  struct Tile {
+    int n;  // prefix_len - kvb
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
 };
 
 // Valid prefix of a KV cache: kv < kv_len[b].
@@ -94,6 +120,11 @@ struct MaskKvLen {
     __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
   };
   static __device__ __forceinline__ Row row(const MaskParams& p, int b, int, int) { return {p.kv_len[b]}; }
+  struct Tile {
+    int n;  // kv_len[b] - kvb
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
 };
 
 // Logical fusion (paper review §4.4; Concepts "Composing masks").
@@ -108,6 +139,12 @@ struct MaskAnd {
   static __device__ __forceinline__ Row row(const MaskParams& p, int b, int h, int q) {
     return {A::row(p, b, h, q), B::row(p, b, h, q)};
   }
+  struct Tile {
+    typename A::Tile a;
+    typename B::Tile b;
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) && B::keep(t.b, cr); }
 };
 
 template <class A, class B>
@@ -121,6 +158,12 @@ struct MaskOr {
   static __device__ __forceinline__ Row row(const MaskParams& p, int b, int h, int q) {
     return {A::row(p, b, h, q), B::row(p, b, h, q)};
   }
+  struct Tile {
+    typename A::Tile a;
+    typename B::Tile b;
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
+  static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) || B::keep(t.b, cr); }
 };
 
 using MaskSlidingCausal = MaskAnd<MaskCausal, MaskWindow>;
@@ -146,18 +189,24 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 // ---------------------------------------------------------------------------
 // score_mods, producing base-2 scores x2 = mod(s) * log2(e).
 //
-// `s` is the raw dot product Q.K (not yet scaled).  apply4 handles four
-// consecutive keys kv0..kv0+3 of one query row; `Tile` carries values a
-// functor wants loaded before the score matrix is ready (the bias tensor).
+// `s` is the raw dot product Q.K (not yet scaled).  apply1(row, s, kv) gives
+// x2 for one key.  The forward's tile form gives y = x2 - m_ref directly,
+// folding the softmax reference max m_ref into the additive term, so the
+// exponential needs no separate subtraction: tile(row, kvb, m_ref), then
+// apply(tile, s, cr) for key kvb + cr.
 // ---------------------------------------------------------------------------
 
 struct ScoreNone {
   struct Row {
     float c;
   };
-  struct Tile {};
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) { return {p.scale_log2}; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) { return s * r.c; }
+  struct Tile {
+    float c, add;
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int, float m_ref) { return {r.c, -m_ref}; }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int) { return fmaf(s, t.c, t.add); }
 };
 
 // Concepts "score_mod": s + slope[h] * (kv - q).
@@ -173,6 +222,15 @@ struct ScoreAlibi {
   }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, r.sl * (float)(kv - r.q));
+  }
+  struct Tile {
+    float c, sl, add;  // add = sl * (kvb - q) - m_ref
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb, float m_ref) {
+    return {r.c, r.sl, fmaf(r.sl, (float)(kvb - r.q), -m_ref)};
+  }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
+    return fmaf(s, t.c, fmaf(t.sl, (float)cr, t.add));
   }
 };
 
@@ -191,6 +249,16 @@ struct ScoreSoftcap {
     float e = __builtin_amdgcn_exp2f(s * r.k);
     return fmaf(-2.0f * r.c2, __builtin_amdgcn_rcpf(1.0f + e), r.c2);
   }
+  struct Tile {
+    float k, neg2c2, add;  // add = cap*log2e - m_ref
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int, float m_ref) {
+    return {r.k, -2.0f * r.c2, r.c2 - m_ref};
+  }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int) {
+    const float e = __builtin_amdgcn_exp2f(s * t.k);
+    return fmaf(t.neg2c2, __builtin_amdgcn_rcpf(1.0f + e), t.add);
+  }
 };
 
 // Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
@@ -202,6 +270,15 @@ struct ScoreRelPos {
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int q) { return {p.scale_log2, q}; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, kLog2e * (float)(r.q - kv));
+  }
+  struct Tile {
+    float c, add;  // add = log2e * (q - kvb) - m_ref
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb, float m_ref) {
+    return {r.c, fmaf(kLog2e, (float)(r.q - kvb), -m_ref)};
+  }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
+    return fmaf(s, t.c, fmaf(-kLog2e, (float)cr, t.add));
   }
 };
 
@@ -216,6 +293,16 @@ struct ScoreBias {
   }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(kLog2e, bf16_bits_to_float(r.row[kv]), s * r.c);
+  }
+  struct Tile {
+    float c, add;
+    const uint16_t* row;  // bias[b, h, q, kvb:]
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int kvb, float m_ref) {
+    return {r.c, -m_ref, r.row + kvb};
+  }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
+    return fmaf(s, t.c, fmaf(kLog2e, bf16_bits_to_float(t.row[cr]), t.add));
   }
 };
 
