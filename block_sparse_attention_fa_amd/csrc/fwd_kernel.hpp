@@ -9,8 +9,8 @@
 //
 // Work decomposition: one 256-thread workgroup (4 waves) per (b, hq, 128-row
 // query tile); wave w owns query rows 32w..32w+31.  Two workgroups share a CU
-// (<= 256 registers per lane, 64 KiB of LDS each), so one workgroup's matrix
-// work overlaps the other's softmax, loads and barriers.
+// (<= 256 registers per lane, 80 KiB of LDS each at D=128), so one workgroup's
+// LDS waits and barriers are covered by the other.
 //
 // MFMA orientation.  Both products are computed transposed so that every
 // lane owns exactly one query row (lane % 32) in both accumulators:
@@ -18,20 +18,24 @@
 //   O^T[d, q] += V^T[d, kv] . P^T[kv, q] (A = V^T read transposed from LDS, B = P^T)
 // with v_mfma_f32_32x32x16_bf16.  In a 32x32 accumulator lane l holds column
 // l % 32 and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  So the softmax row
-// max and row sum reduce over the lane's own 64 values plus one swap with
-// lane l ^ 32, the O rescale is a per-lane scalar, and the P values leave the
-// S accumulator already laid out as the B operand of the PV product: the 16
+// max and row sum reduce over the lane's own values plus one swap with lane
+// l ^ 32, the O rescale is a per-lane scalar, and the P values leave the S
+// accumulator already laid out as the B operand of the PV product: the 16
 // keys of a PV k-step sit in lane half h at kv = 4h + {0..3} and 8 + 4h + {0..3}.
 // The matching V^T operand comes from row-major V in LDS through
 // ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
 // of the 8-byte row pointed to by lane 4j + i/4 (j = 0..3), so lanes pointing
 // at a 4-key x 16-dim block of V receive one dim each across the 4 keys.
 //
-// Data movement: K and V tiles go from global memory straight into LDS with
-// 16-byte global_load_lds (no registers), row-major with the 16-byte chunks
-// of each row XOR-swizzled (bank-conflict-free reads, see k_swizzle/v_swizzle).  The K tile
-// of step t+1 streams in during the softmax and PV of step t; the V tile of
-// step t+1 during QK^T and softmax of step t+1.
+// Software pipeline.  On gfx950 a wave's VALU work only overlaps MFMAs that
+// the same wave has in flight (measured: none across waves of a SIMD), so
+// each 64-key step pairs the score VALU of sub-tile j with the PV MFMAs of
+// sub-tile j-1, and the exponentials of j with the QK^T MFMAs of j+1.
+//
+// Data movement: K and V sub-tiles go from global memory straight into LDS
+// with 16-byte global_load_lds (no registers), row-major with the 16-byte
+// chunks of each row XOR-swizzled (bank-conflict-free reads, see
+// k_swizzle/v_swizzle), in a 2-deep K ring and a 3-deep V ring.
 #pragma once
 
 #include <type_traits>
@@ -129,16 +133,18 @@ void fwd_kernel(FwdParams p) {
   constexpr int KS = D / 16;                  // k-steps of the QK^T product
   constexpr int DT = D / 32;                  // 32-row blocks of O^T
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int HB = 64;                      // keys per sub-tile (half a BlockMask tile)
-  constexpr int NI = HB * CPR / 64 / 4;       // 16-byte loads per wave per sub-tile buffer
-  // two stages of K and V sub-tiles, row-major, chunks XOR-swizzled by row
-  __shared__ __align__(16) uint16_t k_lds[2][HB * D];
-  __shared__ __align__(16) uint16_t v_lds[2][HB * D];
+  constexpr int HB = 64;                      // keys per step (half a BlockMask tile)
+  constexpr int SPT = kBN / HB;               // steps per BlockMask tile
+  constexpr int NI = HB * CPR / 64 / 4;       // 16-byte loads per wave per K or V sub-tile
+  constexpr int NK = 2, NV = 3;               // ring depths: K of j+1 / j+2, V of j-1 / j / j+1
+  __shared__ __align__(16) uint16_t k_lds[NK][HB * D];
+  __shared__ __align__(16) uint16_t v_lds[NV][HB * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int lq = lane & 31, hh = lane >> 5;
+  const int gi = lane >> 4, si = lane & 15;
 
   // ---- which (b, hq, query tile) ------------------------------------------
   const int NQ = (p.Sq + kBM - 1) / kBM;
@@ -183,29 +189,29 @@ void fwd_kernel(FwdParams p) {
   const long long ks2 = p.ks[2], vs2 = p.vs[2];
 
   // ---- global -> LDS sub-tile loads -------------------------------------------
-  // Sub-tile j = keys [64 (j % 2), 64 (j % 2) + 64) of BlockMask tile kb_of(j / 2).
-  // LDS slot s (16 bytes) holds row s / CPR, logical chunk (s % CPR) ^ swizzle(row);
-  // wave w issues slots [64 (4i + w), +64) for i < NI.  Rows past Skv re-read
-  // row Skv-1 (finite values whose scores are masked to -inf).
-  // Within one instruction the 64 lanes cover 64 / CPR consecutive rows; the
-  // swizzled chunk of a lane does not depend on i (the swizzles only use row
-  // bits below 4 * RPI), so a per-lane offset plus a uniform row step per
+  // Sub-tile j = keys [64 (j % 2), 64 (j % 2) + 64) of BlockMask tile kb_of(j / 2);
+  // K of j lives in K stage j % 2, V of j in V stage j % 3.  LDS slot s (16 bytes)
+  // of a stage holds row s / CPR, logical chunk (s % CPR) ^ swizzle(row); wave w
+  // issues slots [64 (4i + w), +64) for i < NI.  Rows past Skv re-read row Skv-1
+  // (finite values whose scores are masked to -inf).  Within one instruction the
+  // 64 lanes cover 64 / CPR consecutive rows and the swizzled chunk of a lane does
+  // not depend on i, so one per-lane byte offset plus a uniform row step per
   // instruction addresses every load.
-  constexpr int RPI = 64 / CPR;                                  // rows per instruction
-  const int lrow = wave * RPI + lane / CPR;                      // row of this lane in instruction 0
-  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);          // logical chunks it loads
+  constexpr int RPI = 64 / CPR;
+  const int lrow = wave * RPI + lane / CPR;
+  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
   const int vchunk = (lane % CPR) ^ v_swizzle<D>(lrow);
-  const uint32_t k_voff = (uint32_t)(2 * lrow * ks2 + 16 * kchunk);  // bytes
+  const uint32_t k_voff = (uint32_t)(2 * lrow * ks2 + 16 * kchunk);
   const uint32_t v_voff = (uint32_t)(2 * lrow * vs2 + 16 * vchunk);
-  auto issue = [&](const uint16_t* g, long long rs, const uint16_t* buf, int lchunk, uint32_t voff, int j) {
-    const int kv0 = kb_of(j >> 1) * kBN + HB * (j & 1);
+  auto issue_one = [&](const uint16_t* g, long long rs, const uint16_t* buf, int lchunk, uint32_t voff,
+                       int kv0) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf)) + 16 * 64 * wave;
     if (kv0 + HB <= p.Skv) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         dma16s(voff, uniform_ptr(g + (long long)(kv0 + 4 * RPI * i) * rs), base + 16 * 64 * 4 * i);
     } else {
-      const int last = p.Skv - 1 - kv0;  // rows past Skv re-read row Skv-1
+      const int last = p.Skv - 1 - kv0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int rr = min(lrow + 4 * RPI * i, last);
@@ -213,7 +219,9 @@ void fwd_kernel(FwdParams p) {
       }
     }
   };
-  // element offsets of (row, logical chunk) in the K and V stages
+  auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
+  auto issue_k = [&](int j) { issue_one(Kp, ks2, k_lds[j % NK], kchunk, k_voff, kv0_of(j)); };
+  auto issue_v = [&](int j) { issue_one(Vp, vs2, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
   auto v_off = [](int r, int chunk) { return r * D + ((chunk ^ v_swizzle<D>(r)) * 8); };
 
@@ -239,141 +247,151 @@ void fwd_kernel(FwdParams p) {
   // then only raised when a score exceeds it by more than kRescaleSlack.  Scores
   // are produced relative to it (y = x2 - m_run), so exp2(y) needs no subtraction.
   float m_run = -INFINITY;
-  float l_run = 0.0f;       // this lane's half of the row sum
+  float l_run = 0.0f;  // this lane's half of the row sum
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute_subtile = [&](int j, int kb, bool partial) {
-    const int buf = j & 1;
-    const int kvt0 = kb * kBN + HB * (j & 1);
-    const bool ragged = kvt0 + HB > p.Skv;
-    const uint16_t* kl = k_lds[buf];
-    const uint16_t* vl = v_lds[buf];
+  // MFMA i (0..2*KS-1) of S^T = K Q^T for a 64-key sub-tile: (32-key block i / KS, k-step i % KS)
+  auto qk_mfma = [&](const uint16_t* kl, f32x16_t (&acc)[2], int i) {
+    const int mt = i / KS, s = i % KS;
+    const bf16x8_t a = *(const bf16x8_t*)&kl[k_off(32 * mt + lq, 2 * s + hh)];
+    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], acc[mt], 0, 0, 0);
+  };
+  // MFMA i (0..4*DT-1) of O^T += V^T P^T: (16-key k-step i / DT of the sub-tile, d block i % DT).
+  // V^T comes from row-major V through ds_read_b64_tr_b16.
+  auto pv_mfma = [&](const uint16_t* vl, const bf16x8_t (&pb)[4], int i) {
+    const int ks = i / DT, dt = i % DT;
+    const int row0 = 16 * ks + 4 * hh + (si >> 2);
+    const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + v_off(row0, d >> 3) + (d & 7)));
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + v_off(row0 + 8, d >> 3) + (d & 7)));
+    const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[dt], 0, 0, 0);
+  };
 
-    // S^T = K Q^T  (2 blocks of 32 keys)
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16_t{};
-      const int r = 32 * mt + lq;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8_t a = *(const bf16x8_t*)&kl[k_off(r, 2 * s + hh)];
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[mt], 0, 0, 0);
-      }
+  // Software pipeline (per wave), step j:
+  //   B: score_mod / mask / row max of sub-tile j     interleaved with  O += PV of sub-tile j-1
+  //   C: (rare) raise the reference max: rescale O (which now includes j-1) and the scores
+  //   D: P = exp2(scores) of sub-tile j, row sums     interleaved with  S = QK^T of sub-tile j+1
+  // so every stretch of VALU work has independent MFMAs of the same wave beside
+  // it.  Loads run ahead: K of j+2 and V of j+1 are issued at the start of step j.
+  const int J = SPT * T;
+  if (J > 0) {
+    // V stage 2 stands in for "sub-tile -1" (P = 0) at step 0: clear it
+    {
+      u32x4_t* vz = (u32x4_t*)v_lds[NV - 1];
+      for (int i = tid; i < HB * D / 8; i += kFwdThreads) vz[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    issue_k(0);
+    if (J > 1) issue_k(1);
+    issue_v(0);
+    if (J > 1)
+      wait_vmcnt<2 * NI>();  // K(0) landed (K(1), V(0) may be in flight)
+    else
+      wait_vmcnt<NI>();
+    wait_lds_reads();
+    __syncthreads();
+    f32x16_t s_cur[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) qk_mfma(k_lds[0], s_cur, i);
+    bf16x8_t p_prev[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p_prev[i] = bf16x8_t{};
 
-    // Element (mt, r) of this lane holds key kvb + cr, cr = 32 mt + 8 (r/4) + r%4.
-    // score_mod everywhere; mask_mod on partial tiles; keys past Skv on the ragged tile.
-    const int kvb = kvt0 + 4 * hh;
-    const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
-    const auto st = Score::tile(srow, kvb, m_ref);
-    float ymax = -INFINITY;
-    if (!partial && !ragged) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-          const float y = Score::apply(st, sacc[mt][r], cr);
-          sacc[mt][r] = y;
-          ymax = fmaxf(ymax, y);
-        }
-      }
-    } else {
-      const auto mtl = Mask::tile(mrow, kvb);
+    for (int j = 0; j < J; ++j) {
+      // K(j+1) and V(j-1) landed for every wave (only V(j) may be in flight), and
+      // every wave is done with step j-1: K stage j % 2 and V stage (j+1) % 3 are free.
+      wait_vmcnt<NI>();
+      wait_lds_reads();
+      __builtin_amdgcn_s_barrier();
+      if (j + 2 < J) issue_k(j + 2);
+      if (j + 1 < J) issue_v(j + 1);
+
+      const int t = j / SPT;
+      const int kvt0 = kb_of(t) * kBN + HB * (j % SPT);
+      const bool partial = t < n_part;
+      const bool ragged = kvt0 + HB > p.Skv;
+      const uint16_t* vprev = v_lds[(j + NV - 1) % NV];
+      const uint16_t* knext = k_lds[(j + 1) % NK];  // stale on the last step (result unused)
+
+      // ---- B: scores of j  ||  PV of j-1
+      // Element (mt, r) of this lane holds key kvb + cr, cr = 32 mt + 8 (r/4) + r%4.
+      const int kvb = kvt0 + 4 * hh;
+      const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
+      const auto st = Score::tile(srow, kvb, m_ref);
       const int lim = ragged ? p.Skv - kvb : HB;  // key kvb + cr exists iff cr < lim
+      float ymax = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int e = 0; e < 32; ++e) {
+        const int mt = e >> 4, r = e & 15;
+        const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+        // functors that read memory get an in-bounds key on the ragged tile
+        const float y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
+        s_cur[mt][r] = y;
+        ymax = fmaxf(ymax, y);
+        if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(vprev, p_prev, e >> 1);
+      }
+      if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
+        const auto mtl = Mask::tile(mrow, kvb);
+        ymax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int e = 0; e < 32; ++e) {
+          const int mt = e >> 4, r = e & 15;
           const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-          const int crs = min(cr, lim - 1);  // in-bounds index for functors that load
           bool keep = cr < lim;
-          if (partial) keep = keep && Mask::keep(mtl, crs);
-          const float y = keep ? Score::apply(st, sacc[mt][r], crs) : -INFINITY;
-          sacc[mt][r] = y;
+          if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+          const float y = keep ? s_cur[mt][r] : -INFINITY;
+          s_cur[mt][r] = y;
           ymax = fmaxf(ymax, y);
         }
       }
-    }
-    ymax = fmaxf(ymax, __shfl_xor(ymax, 32));
-    const bool raise = ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY);
-    if (__any(raise)) {
-      const float m_new = fmaxf(m_run, m_ref + ymax);
-      const float shift = m_new == -INFINITY ? 0.0f : m_ref - m_new;
-      const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sacc[mt] += shift;
-      m_run = m_new;
-    }
+      for (int i = 16; i < 4 * DT; ++i) pv_mfma(vprev, p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
 
-    // P = exp2(y) in bf16; the row sum adds the rounded values (v_dot2 with ones)
-    bf16x8_t pb[2][2];
+      // ---- C: raise the reference max when needed
+      ymax = fmaxf(ymax, __shfl_xor(ymax, 32));
+      const bool raise = ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY);
+      if (__any(raise)) {
+        const float m_new = fmaxf(m_run, m_ref + ymax);
+        const float shift = m_new == -INFINITY ? 0.0f : m_ref - m_new;
+        const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+        for (int mt = 0; mt < 2; ++mt) s_cur[mt] += shift;
+        m_run = m_new;
+      }
+
+      // ---- D: P of j  ||  S of j+1
+      f32x16_t s_nxt[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {  // 16-key k-step g of the PV product
+        const int mt = g >> 1, h8 = 8 * (g & 1);
         bf16x2_t pk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          pk[k][0] = (__bf16)__builtin_amdgcn_exp2f(sacc[mt][8 * s + 2 * k]);
-          pk[k][1] = (__bf16)__builtin_amdgcn_exp2f(sacc[mt][8 * s + 2 * k + 1]);
+          pk[k][0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k]);
+          pk[k][1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k + 1]);
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, l_run, false);
+          qk_mfma(knext, s_nxt, 4 * g + k);
         }
-        pb[mt][s] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+        p_prev[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                             __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
                                             0, 1, 2, 3, 4, 5, 6, 7);
       }
-    }
-
-    // O^T += V^T P^T
-    const int gi = lane >> 4, si = lane & 15;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int row0 = 32 * mt + 16 * s + 4 * hh + (si >> 2);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
-          const int off_lo = v_off(row0, d >> 3) + (d & 7);
-          const int off_hi = v_off(row0 + 8, d >> 3) + (d & 7);
-          const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_lo));
-          const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + off_hi));
-          const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mt][s], oacc[dt], 0, 0, 0);
-        }
-      }
+      for (int i = 16; i < 2 * KS; ++i) qk_mfma(knext, s_nxt, i);  // (D=128 has 16 QK MFMAs: none left)
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
     }
-  };
-
-  const int J = 2 * T;
-  if (J > 0) {
-    issue(Kp, ks2, k_lds[0], kchunk, k_voff, 0);
-    issue(Vp, vs2, v_lds[0], vchunk, v_voff, 0);
-    issue(Kp, ks2, k_lds[1], kchunk, k_voff, 1);
-    issue(Vp, vs2, v_lds[1], vchunk, v_voff, 1);
-    for (int j = 0; j < J; ++j) {
-      // K(j), V(j) landed for every wave; K(j+1), V(j+1) may still be in flight
-      if (j + 1 < J)
-        wait_vmcnt<2 * NI>();
-      else
-        wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      const int t = j >> 1;
-      compute_subtile(j, kb_of(t), t < n_part);
-      // every wave is done reading stage j % 2: refill it with sub-tile j + 2
-      wait_lds_reads();
-      __builtin_amdgcn_s_barrier();
-      if (j + 2 < J) {
-        issue(Kp, ks2, k_lds[j & 1], kchunk, k_voff, j + 2);
-        issue(Vp, vs2, v_lds[j & 1], vchunk, v_voff, j + 2);
-      }
-    }
+    // PV of the last sub-tile
+    wait_vmcnt<0>();
+    wait_lds_reads();
+    __builtin_amdgcn_s_barrier();
+    const uint16_t* vlast = v_lds[(J - 1) % NV];
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) pv_mfma(vlast, p_prev, i);
   }
 
   // ---- epilogue ---------------------------------------------------------------

@@ -197,6 +197,7 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 // ---------------------------------------------------------------------------
 
 struct ScoreNone {
+  static constexpr bool kReadsMemory = false;
   struct Row {
     float c;
   };
@@ -211,6 +212,7 @@ struct ScoreNone {
 
 // Concepts "score_mod": s + slope[h] * (kv - q).
 struct ScoreAlibi {
+  static constexpr bool kReadsMemory = false;
   struct Row {
     float c;    // scale * log2e
     float sl;   // slope[h] * log2e
@@ -238,6 +240,7 @@ struct ScoreAlibi {
 // tanh(y) = 1 - 2 / (1 + e^{2y}) evaluated with the hardware exp2 and
 // reciprocal; the error this adds is measured against fp64 tanh in the tests.
 struct ScoreSoftcap {
+  static constexpr bool kReadsMemory = false;
   struct Row {
     float k;     // 2 * scale / cap * log2e
     float c2;    // cap * log2e
@@ -263,6 +266,7 @@ struct ScoreSoftcap {
 
 // Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
 struct ScoreRelPos {
+  static constexpr bool kReadsMemory = false;
   struct Row {
     float c;
     int q;
@@ -284,6 +288,7 @@ struct ScoreRelPos {
 
 // Dynamic-bias feature request (attention-gym issue 123): s + bias[b,h,q,kv].
 struct ScoreBias {
+  static constexpr bool kReadsMemory = true;
   struct Row {
     float c;
     const uint16_t* row;  // bias[b, h, q, :]
