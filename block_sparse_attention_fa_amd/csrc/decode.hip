@@ -7,13 +7,13 @@
 // the score_mod still applies.  The chunks are cut from the sequence's
 // BlockMask row (partial tiles first, then full tiles), so empty tiles past a
 // sequence's valid length are never read (Concepts page, "BlockMask
-// Internals").
+// Internals").  A chunk is every splits-th entry of that list.
 //
 // decode_partial: one 256-thread workgroup per (split, KV head, batch row).
 // It reads each K/V row of its chunk exactly once and serves all G query
 // heads of that KV head from it (GQA).  Pass 1 computes the G scores of every
 // key into LDS (16-byte row loads, a dot product per lane over 8 dims and a
-// cross-lane sum), pass 2 takes each head's max and exponentials, pass 3
+// DPP sum over the lanes of the row), pass 2 takes each head's max and exponentials, pass 3
 // accumulates P.V.  Its output is the chunk's normalised partial output and
 // base-2 LSE in a caller-provided fp32 workspace.
 // decode_merge: LSE = log-sum-exp of the chunk LSEs, O = sum_s e^(LSE_s - LSE) O_s.
@@ -45,6 +45,19 @@ __device__ __forceinline__ void unpack8(const u32x4_t& x, float (&f)[8]) {
     f[2 * i] = __uint_as_float(x[i] << 16);
     f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
   }
+}
+
+// Sum over groups of LPR (8 or 16) consecutive lanes, result in every lane of
+// the group, with DPP moves (no LDS traffic): quad xor 1, quad xor 2, half-row
+// mirror, and for 16 lanes the row mirror.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if (LPR == 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
 }
 
 template <int D, int G, class Score>
@@ -82,14 +95,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     }
   }
   const int T = n_part + n_full;
-  const int t0 = split * P.blocks_per_split;
-  const int t1 = min(T, t0 + P.blocks_per_split);
+  // Tiles are dealt to the splits round-robin (split s takes list entries s,
+  // s + splits, ...), so the workgroups that run together read neighbouring
+  // tiles instead of addresses a power-of-two stride apart.
+  const int n_tiles = T > split ? (T - split + P.splits - 1) / P.splits : 0;
   const long long ws_row0 = ((long long)b * p.Hq + (long long)hkv * G) * P.splits + split;
-  if (t0 >= t1) {
+  if (n_tiles == 0) {
     if (tid < G) P.ws_lse[ws_row0 + (long long)tid * P.splits] = -INFINITY;
     return;
   }
-  const int n_rows = (t1 - t0) * FA_BLOCK;
+  const int n_rows = n_tiles * FA_BLOCK;
+  auto tile_of = [&](int rl) { return split + min(rl / FA_BLOCK, n_tiles - 1) * P.splits; };
   auto kb_of = [&](int t) -> int {
     if (t < n_part) return part_idx[t];
     return bm.dense ? (t - n_part) : full_idx[t - n_part];
@@ -118,8 +134,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rl = base + u * RSTEP + wave * RPW + rr;
-      const int t = t0 + rl / FA_BLOCK;
-      const int kv = kb_of(min(t, t1 - 1)) * FA_BLOCK + rl % FA_BLOCK;
+      const int t = tile_of(rl);
+      const int kv = kb_of(t) * FA_BLOCK + rl % FA_BLOCK;
       kvs[u] = kv;
       part[u] = t < n_part;
       u32x4_t x = {0u, 0u, 0u, 0u};
@@ -140,10 +156,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         dot[g] = a;
       }
 #pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) dot[g] += __shfl_xor(dot[g], off);
-      }
+      for (int g = 0; g < G; ++g) dot[g] = group_sum<LPR>(dot[g]);
       const int kv = kvs[u];
       bool keep = kv < p.Skv;
       if (keep && part[u]) {
@@ -215,8 +228,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rl = base + u * RSTEP + wave * RPW + rr;
-      const int t = t0 + rl / FA_BLOCK;
-      const int kv = kb_of(min(t, t1 - 1)) * FA_BLOCK + rl % FA_BLOCK;
+      const int kv = kb_of(tile_of(rl)) * FA_BLOCK + rl % FA_BLOCK;
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (rl < n_rows && kv < p.Skv) x = *(const u32x4_t*)(Vp + (long long)kv * p.vs[2] + 8 * sub);
       vx[u] = x;

@@ -187,9 +187,10 @@ DecodePlan decode_plan(const fa_attn_args* a) {
   if (a->num_splits > 0) {
     bps = ceil_div(NK, a->num_splits);
   } else {
-    // Enough workgroups to cover the 256 CUs several times over.
-    bps = 8;
-    while (bps > 1 && (long long)a->B * a->Hkv * ceil_div(NK, bps) < 2048) bps /= 2;
+    // Six tiles per chunk (measured best for long caches), fewer while the
+    // grid would not cover the 256 CUs many times over.
+    bps = 6;
+    while (bps > 1 && (long long)a->B * a->Hkv * ceil_div(NK, bps) < 4096) --bps;
   }
   if (bps < 1) bps = 1;
   if (bps > 8) bps = 8;

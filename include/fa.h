@@ -188,7 +188,8 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
 /* Split-KV decode (talk summary, "Flex Decoding": split along the key axis
  * for parallelism, then a final reduction; score_mod still applies).  Sq must
  * be 1; the query sits at q index 0.  Each sequence's block list (its
- * BlockMask row) is cut into chunks; one workgroup per (chunk, KV head, batch
+ * BlockMask row) is dealt round-robin into chunks (chunk s holds entries s,
+ * s + splits, s + 2 splits, ...); one workgroup per (chunk, KV head, batch
  * row) computes all Hq/Hkv query heads of that KV head against the chunk, and
  * a merge kernel combines the chunks through their log-sum-exp.  The result
  * does not depend on the split count beyond fp32 rounding.  The GQA group

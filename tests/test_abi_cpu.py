@@ -134,12 +134,18 @@ def test_decode_validation_and_workspace_size():
     a = _args(B=2, Hq=8, Hkv=2, Sq=1, Skv=5000, D=128)
     n = ctypes.c_size_t()
     assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
-    NK = 40
-    bps = 8
-    while bps > 1 and 2 * 2 * -(-NK // bps) < 2048:
-        bps //= 2
-    splits = -(-NK // bps)
-    assert n.value == splits * 2 * 8 * (128 + 1) * 4
+    # 40 kv tiles, B*Hkv = 4: the automatic plan shrinks chunks to one tile
+    # (the grid stays below 4096 workgroups), so 40 splits.
+    assert n.value == 40 * 2 * 8 * (128 + 1) * 4
+    # explicit num_splits: chunk = clamp(ceil(40 / n), 1, 8) tiles, splits = ceil(40 / chunk)
+    for ns, splits in ((7, 7), (3, 5), (40, 40), (100, 40), (1, 5)):
+        a.num_splits = ns
+        assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+        assert n.value == splits * 2 * 8 * (128 + 1) * 4, ns
+    a.num_splits = 0
+    a.B, a.Hkv, a.Hq, a.Skv = 32, 8, 32, 32768  # 256 tiles, 256 (b, kv head) pairs: 6-tile chunks
+    assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    assert n.value == 43 * 32 * 32 * (128 + 1) * 4
     a = _args(Sq=2)
     assert _status(a, decode=True) == fa.FA_ERR_SHAPE
     a = _args(Hq=6, Hkv=2, Sq=1)
