@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain fp16->bf16 copies of MIB MiB each (reads MIB MiB, writes "
+                         "MIB MiB): the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -110,6 +113,17 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 19  # 2-byte elements
+        src = torch.zeros(n, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"kernel": "fp16->bf16 elementwise copy", "launches": 5,
+                                               "read_bytes_per_launch": 2 * n,
+                                               "write_bytes_per_launch": 2 * n}}), flush=True)
+        return
     from block_sparse_attention_fa_amd import fa
     from block_sparse_attention_fa_amd import inputs as gen
 
