@@ -50,6 +50,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
 constexpr int kFwdThreads = 256;
 constexpr int kBM = FA_BLOCK;  // query rows per workgroup
@@ -100,14 +101,6 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
                :: "v"(voff), "s"(sbase), "s"(lds));
 }
 
-// A pointer the compiler can keep in SGPRs (the value is the same in every lane).
-__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
-  const uint64_t v = (uint64_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(((uint64_t)hi << 32) | lo);
-}
-
 // LDS swizzles (16-byte chunk index XOR a function of the row), chosen per
 // read pattern so that each group of lanes served together touches distinct
 // banks (64 banks of 4 bytes: a 256-byte window):
@@ -124,6 +117,23 @@ __device__ __forceinline__ int k_swizzle(int r) {
 template <int D>
 __device__ __forceinline__ int v_swizzle(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Marks a register as produced here, after waiting for the load that wrote
+// it: later readers then need no wait of their own (without this the
+// compiler, unsure whether a load issued on an earlier iteration is still in
+// flight, puts a vmcnt(0) before every read, which also waits for the tile
+// loads).
+__device__ __forceinline__ void loaded(int& x) { asm volatile("" : "+v"(x)); }
+
+// max(x, x of lane l ^ 32) in every lane, with v_permlane32_swap (swaps the
+// upper half of one register with the lower half of another; no LDS access).
+// Written as asm: the compiler's builtin for it returns the same register for
+// both halves of its result.  The s_nop covers the VALU-write hazard.
+__device__ __forceinline__ float max_across_halves(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 template <int D, class Mask, class Score>
@@ -178,15 +188,24 @@ void fwd_kernel(FwdParams p) {
     }
   }
   const int T = n_part + n_full;
-  auto kb_of = [&](int t) -> int {
-    if (t < n_part) return part_idx[t];
-    return bm.dense ? (t - n_part) : full_idx[t - n_part];
+  // List entry e of this row (partial tiles, then full tiles; 0 past the end).
+  auto list_entry = [&](int e) -> int {
+    if (e >= T) return 0;
+    if (e < n_part) return part_idx[e];
+    return bm.dense ? e - n_part : full_idx[e - n_part];
   };
+  // A window of 64 list entries lives in one register (lane i: entry win0 + i)
+  // and is read back with readlane, so the per-step block lookups touch no
+  // memory and never wait on the tile loads in flight.
+  int win0 = 0;
+  int win = list_entry(lane);
+  loaded(win);
+  auto kb_of = [&](int t) -> int { return __builtin_amdgcn_readlane(win, t - win0); };
 
   const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1];
-  const uint16_t* Kp = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1];
-  const uint16_t* Vp = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1];
-  const long long ks2 = p.ks[2], vs2 = p.vs[2];
+  const char* Kp = (const char*)(p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1]);
+  const char* Vp = (const char*)(p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1]);
+  const long long ksb = 2 * p.ks[2], vsb = 2 * p.vs[2];  // row strides in bytes
 
   // ---- global -> LDS sub-tile loads -------------------------------------------
   // Sub-tile j = keys [64 (j % 2), 64 (j % 2) + 64) of BlockMask tile kb_of(j / 2);
@@ -201,27 +220,26 @@ void fwd_kernel(FwdParams p) {
   const int lrow = wave * RPI + lane / CPR;
   const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
   const int vchunk = (lane % CPR) ^ v_swizzle<D>(lrow);
-  const uint32_t k_voff = (uint32_t)(2 * lrow * ks2 + 16 * kchunk);
-  const uint32_t v_voff = (uint32_t)(2 * lrow * vs2 + 16 * vchunk);
-  auto issue_one = [&](const uint16_t* g, long long rs, const uint16_t* buf, int lchunk, uint32_t voff,
-                       int kv0) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf)) + 16 * 64 * wave;
+  const uint32_t k_voff = (uint32_t)(lrow * ksb + 16 * kchunk);
+  const uint32_t v_voff = (uint32_t)(lrow * vsb + 16 * vchunk);
+  auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, int lchunk, uint32_t voff, int kv0) {
+    const uint32_t base = lds_address(buf) + 16 * 64 * wave;
     if (kv0 + HB <= p.Skv) {
+      const char* g0 = g + kv0 * rsb;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        dma16s(voff, uniform_ptr(g + (long long)(kv0 + 4 * RPI * i) * rs), base + 16 * 64 * 4 * i);
+      for (int i = 0; i < NI; ++i) dma16s(voff, g0 + 4 * RPI * i * rsb, base + 16 * 64 * 4 * i);
     } else {
       const int last = p.Skv - 1 - kv0;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int rr = min(lrow + 4 * RPI * i, last);
-        dma16(g + (long long)(kv0 + rr) * rs + 8 * lchunk, base + 16 * 64 * 4 * i);
+        dma16(g + (kv0 + rr) * rsb + 16 * lchunk, base + 16 * 64 * 4 * i);
       }
     }
   };
   auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
-  auto issue_k = [&](int j) { issue_one(Kp, ks2, k_lds[j % NK], kchunk, k_voff, kv0_of(j)); };
-  auto issue_v = [&](int j) { issue_one(Vp, vs2, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
+  auto issue_k = [&](int j) { issue_one(Kp, ksb, k_lds[j % NK], kchunk, k_voff, kv0_of(j)); };
+  auto issue_v = [&](int j) { issue_one(Vp, vsb, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
   auto v_off = [](int r, int chunk) { return r * D + ((chunk ^ v_swizzle<D>(r)) * 8); };
 
@@ -251,20 +269,45 @@ void fwd_kernel(FwdParams p) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // Per-lane element offsets of the MFMA operands inside a K or V stage.  The
+  // swizzle only depends on the row bits that belong to the lane (32-row
+  // blocks of K, 16-row k-steps and the +8 half of V leave them unchanged), so
+  // every read is a per-lane register plus a compile-time offset, and a stage
+  // change costs one add per register.
+  int koff[KS];  // QK A operand, k-step s: row lq (+32 per key block), chunk 2s + hh
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = k_off(lq, 2 * s + hh);
+  int voff[DT];  // PV A operand, d block dt: rows 4hh + si/4 (+16 per k-step, +8 for the upper half)
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
+    voff[dt] = v_off(4 * hh + (si >> 2), d >> 3) + (d & 7);
+  }
+
+  // Operand reads take a stage's per-lane byte addresses (one register per k-step
+  // of K, one per d block of V, set once per step) plus compile-time offsets.
+  uint32_t kaddr[KS], vaddr[DT];
+  auto set_k_stage = [&](const uint16_t* kl) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kaddr[s] = lds_address(kl) + 2 * koff[s];
+  };
+  auto set_v_stage = [&](const uint16_t* vl) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vaddr[dt] = lds_address(vl) + 2 * voff[dt];
+  };
   // MFMA i (0..2*KS-1) of S^T = K Q^T for a 64-key sub-tile: (32-key block i / KS, k-step i % KS)
-  auto qk_mfma = [&](const uint16_t* kl, f32x16_t (&acc)[2], int i) {
+  auto qk_mfma = [&](f32x16_t (&acc)[2], int i) {
     const int mt = i / KS, s = i % KS;
-    const bf16x8_t a = *(const bf16x8_t*)&kl[k_off(32 * mt + lq, 2 * s + hh)];
+    const bf16x8_t a = ((const lds_bf16x8_t*)(uintptr_t)kaddr[s])[mt * 32 * D / 8];
     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], acc[mt], 0, 0, 0);
   };
   // MFMA i (0..4*DT-1) of O^T += V^T P^T: (16-key k-step i / DT of the sub-tile, d block i % DT).
   // V^T comes from row-major V through ds_read_b64_tr_b16.
-  auto pv_mfma = [&](const uint16_t* vl, const bf16x8_t (&pb)[4], int i) {
+  auto pv_mfma = [&](const bf16x8_t (&pb)[4], int i) {
     const int ks = i / DT, dt = i % DT;
-    const int row0 = 16 * ks + 4 * hh + (si >> 2);
-    const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + v_off(row0, d >> 3) + (d & 7)));
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(vl + v_off(row0 + 8, d >> 3) + (d & 7)));
+    lds_bf16x4_t* vr = (lds_bf16x4_t*)(uintptr_t)vaddr[dt];
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(vr + ks * 16 * D / 4);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(vr + (ks * 16 + 8) * D / 4);
     const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[dt], 0, 0, 0);
   };
@@ -291,28 +334,38 @@ void fwd_kernel(FwdParams p) {
       wait_vmcnt<NI>();
     wait_lds_reads();
     __syncthreads();
-    f32x16_t s_cur[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t s_a[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t s_b[2];
+    set_k_stage(k_lds[0]);
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) qk_mfma(k_lds[0], s_cur, i);
+    for (int i = 0; i < 2 * KS; ++i) qk_mfma(s_a, i);
     bf16x8_t p_prev[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p_prev[i] = bf16x8_t{};
 
+    f32x16_t (&s_cur)[2] = s_a;
+    f32x16_t (&s_nxt)[2] = s_b;
     for (int j = 0; j < J; ++j) {
+      const int H = j % SPT;
       // K(j+1) and V(j-1) landed for every wave (only V(j) may be in flight), and
       // every wave is done with step j-1: K stage j % 2 and V stage (j+1) % 3 are free.
       wait_vmcnt<NI>();
       wait_lds_reads();
       __builtin_amdgcn_s_barrier();
+      const int t = j / SPT;
+      if (t + 1 >= win0 + 64) {  // slide the block-list window (every 64 tiles)
+        win0 = t;
+        win = list_entry(t + lane);
+        loaded(win);
+      }
       if (j + 2 < J) issue_k(j + 2);
       if (j + 1 < J) issue_v(j + 1);
 
-      const int t = j / SPT;
-      const int kvt0 = kb_of(t) * kBN + HB * (j % SPT);
+      const int kvt0 = kb_of(t) * kBN + HB * H;
       const bool partial = t < n_part;
       const bool ragged = kvt0 + HB > p.Skv;
-      const uint16_t* vprev = v_lds[(j + NV - 1) % NV];
-      const uint16_t* knext = k_lds[(j + 1) % NK];  // stale on the last step (result unused)
+      set_v_stage(v_lds[(j + NV - 1) % NV]);  // V of j-1
+      set_k_stage(k_lds[(j + 1) % NK]);       // K of j+1 (stale on the last step: result unused)
 
       // ---- B: scores of j  ||  PV of j-1
       // Element (mt, r) of this lane holds key kvb + cr, cr = 32 mt + 8 (r/4) + r%4.
@@ -329,7 +382,7 @@ void fwd_kernel(FwdParams p) {
         const float y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
         s_cur[mt][r] = y;
         ymax = fmaxf(ymax, y);
-        if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(vprev, p_prev, e >> 1);
+        if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
       }
       if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
         const auto mtl = Mask::tile(mrow, kvb);
@@ -346,10 +399,10 @@ void fwd_kernel(FwdParams p) {
         }
       }
 #pragma unroll
-      for (int i = 16; i < 4 * DT; ++i) pv_mfma(vprev, p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
+      for (int i = 16; i < 4 * DT; ++i) pv_mfma(p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
 
       // ---- C: raise the reference max when needed
-      ymax = fmaxf(ymax, __shfl_xor(ymax, 32));
+      ymax = max_across_halves(ymax);
       const bool raise = ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY);
       if (__any(raise)) {
         const float m_new = fmaxf(m_run, m_ref + ymax);
@@ -364,7 +417,8 @@ void fwd_kernel(FwdParams p) {
       }
 
       // ---- D: P of j  ||  S of j+1
-      f32x16_t s_nxt[2] = {f32x16_t{}, f32x16_t{}};
+      s_nxt[0] = f32x16_t{};
+      s_nxt[1] = f32x16_t{};
 #pragma unroll
       for (int g = 0; g < 4; ++g) {  // 16-key k-step g of the PV product
         const int mt = g >> 1, h8 = 8 * (g & 1);
@@ -374,14 +428,14 @@ void fwd_kernel(FwdParams p) {
           pk[k][0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k]);
           pk[k][1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k + 1]);
           l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, l_run, false);
-          qk_mfma(knext, s_nxt, 4 * g + k);
+          if (4 * g + k < 2 * KS) qk_mfma(s_nxt, 4 * g + k);  // D=64 has 8 QK MFMAs
         }
         p_prev[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                             __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
                                             0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int i = 16; i < 2 * KS; ++i) qk_mfma(knext, s_nxt, i);  // (D=128 has 16 QK MFMAs: none left)
+      for (int i = 16; i < 2 * KS; ++i) qk_mfma(s_nxt, i);  // (D=128 has 16 QK MFMAs: none left)
       s_cur[0] = s_nxt[0];
       s_cur[1] = s_nxt[1];
     }
@@ -389,9 +443,9 @@ void fwd_kernel(FwdParams p) {
     wait_vmcnt<0>();
     wait_lds_reads();
     __builtin_amdgcn_s_barrier();
-    const uint16_t* vlast = v_lds[(J - 1) % NV];
+    set_v_stage(v_lds[(J - 1) % NV]);
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) pv_mfma(vlast, p_prev, i);
+    for (int i = 0; i < 4 * DT; ++i) pv_mfma(p_prev, i);
   }
 
   // ---- epilogue ---------------------------------------------------------------

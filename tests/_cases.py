@@ -13,11 +13,11 @@ from oracle import flex_oracle as fo
 TOL_MAX = 2e-2   # max abs error, bf16 inputs with fp32 accumulation
 TOL_MEAN = 2e-3  # mean abs error
 # LSE (natural log, fp32).  The forward kernel sums the bf16-rounded
-# probabilities it feeds to the PV product, so each term of the row sum l
-# carries a relative error of at most 2^-9 and ln(l) is off by at most
-# ln(1 + 2^-9) < 1.96e-3; fp32 rounding of the scores and of m + ln(l) adds
-# a few ulps of |LSE|.
-LSE_TOL_ABS = 2.5e-3
+# probabilities it feeds to the PV product.  bf16 keeps 8 significant bits,
+# so each term of the row sum l carries a relative error of at most 2^-8 and
+# ln(l) is off by at most -ln(1 - 2^-8) < 3.92e-3; fp32 rounding of the
+# scores and of m + ln(l) adds a few ulps of |LSE|.
+LSE_TOL_ABS = 4e-3
 LSE_TOL_REL = 1e-5
 
 MASK_NAMES = ["none", "causal", "sliding_window", "sliding_causal", "document",
