@@ -11,11 +11,14 @@
 //
 // decode_partial: one 256-thread workgroup per (split, KV head, batch row).
 // It reads each K/V row of its chunk exactly once and serves all G query
-// heads of that KV head from it (GQA).  Pass 1 computes the G scores of every
-// key into LDS (16-byte row loads, a dot product per lane over 8 dims and a
-// DPP sum over the lanes of the row), pass 2 takes each head's max and exponentials, pass 3
-// accumulates P.V.  Its output is the chunk's normalised partial output and
-// base-2 LSE in a caller-provided fp32 workspace.
+// heads of that KV head from it (GQA).  The chunk's tile rows are looked up
+// once into LDS, so no row load waits on a block-list read.  Pass 1 computes
+// the G scores of every key into LDS (16-byte row loads, a dot product per
+// lane over 8 dims and a DPP sum over the lanes of the row), pass 2 takes each
+// head's max and exponentials, pass 3 accumulates P.V; in passes 1 and 3 the
+// next group of rows is loaded while the current one is used, and the first
+// V rows are in flight during pass 2.  Its output is the chunk's normalised
+// partial output and base-2 LSE in a caller-provided fp32 workspace.
 // decode_merge: LSE = log-sum-exp of the chunk LSEs, O = sum_s e^(LSE_s - LSE) O_s.
 #include "mods.hpp"
 
@@ -105,11 +108,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     return;
   }
   const int n_rows = n_tiles * FA_BLOCK;
-  auto tile_of = [&](int rl) { return split + min(rl / FA_BLOCK, n_tiles - 1) * P.splits; };
-  auto kb_of = [&](int t) -> int {
-    if (t < n_part) return part_idx[t];
-    return bm.dense ? (t - n_part) : full_idx[t - n_part];
-  };
+  // First key of each of this chunk's tiles and whether the tile is partial,
+  // looked up once (the row loads below then depend on no global read).
+  __shared__ int s_kv0[kMaxBps];
+  __shared__ int s_part[kMaxBps];
+  if (tid < n_tiles) {
+    const int t = split + tid * P.splits;
+    const int kb = t < n_part ? part_idx[t] : (bm.dense ? t - n_part : full_idx[t - n_part]);
+    s_kv0[tid] = kb * FA_BLOCK;
+    s_part[tid] = t < n_part;
+  }
 
   const uint16_t* Kp = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1];
   const uint16_t* Vp = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1];
@@ -124,27 +132,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   typename Score::Row srow[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) srow[g] = Score::row(p.score, b, hkv * G + g, 0);
+  __syncthreads();
+
+  // An iteration covers STEP consecutive rows of the chunk (inside one tile):
+  // lane group rr of wave w holds rows u * RSTEP + w * RPW + rr, u < U.  The
+  // next iteration's rows are loaded while the current ones are used.
+  constexpr int U = 4;
+  constexpr int STEP = RSTEP * U;
+  static_assert(FA_BLOCK % STEP == 0, "an iteration stays inside one tile");
+  const int my_row = wave * RPW + rr;
+  auto load_rows = [&](const uint16_t* X, long long xs, int base, u32x4_t (&x)[U]) {
+    const int kv0 = s_kv0[base / FA_BLOCK] + base % FA_BLOCK + my_row;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kv = kv0 + u * RSTEP;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (kv < p.Skv) v = *(const u32x4_t*)(X + (long long)kv * xs + 8 * sub);
+      x[u] = v;
+    }
+  };
 
   // ---- pass 1: scores ---------------------------------------------------------
-  constexpr int U = 4;
-  for (int base = 0; base < n_rows; base += RSTEP * U) {
-    u32x4_t kx[U];
-    int kvs[U];
-    bool part[U];
+  auto score_rows = [&](int base, const u32x4_t (&kx)[U]) {
+    const int kv0 = s_kv0[base / FA_BLOCK] + base % FA_BLOCK + my_row;
+    const bool part = s_part[base / FA_BLOCK];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int rl = base + u * RSTEP + wave * RPW + rr;
-      const int t = tile_of(rl);
-      const int kv = kb_of(t) * FA_BLOCK + rl % FA_BLOCK;
-      kvs[u] = kv;
-      part[u] = t < n_part;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (rl < n_rows && kv < p.Skv) x = *(const u32x4_t*)(Kp + (long long)kv * p.ks[2] + 8 * sub);
-      kx[u] = x;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rl = base + u * RSTEP + wave * RPW + rr;
+      const int rl = base + u * RSTEP + my_row;
+      const int kv = kv0 + u * RSTEP;
       float kf[8];
       unpack8(kx[u], kf);
       float dot[G];
@@ -153,18 +168,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         float a = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) a = fmaf(qf[g][j], kf[j], a);
-        dot[g] = a;
+        dot[g] = group_sum<LPR>(a);
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g) dot[g] = group_sum<LPR>(dot[g]);
-      const int kv = kvs[u];
       bool keep = kv < p.Skv;
-      if (keep && part[u]) {
+      if (keep && part) {
         EvalMask em{p.mask, b, hkv * G, 0, kv, false};
         dispatch_mask(P.mask_kind, em);
         keep = em.result;
       }
-      if (rl < n_rows && sub < G) {
+      if (sub < G) {
         float x = -INFINITY;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -173,8 +185,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         sc[sub][rl] = x;
       }
     }
+  };
+  u32x4_t xa[U], xb[U];
+  load_rows(Kp, p.ks[2], 0, xa);
+  for (int base = 0; base < n_rows; base += 2 * STEP) {
+    const bool second = base + STEP < n_rows;
+    if (second) load_rows(Kp, p.ks[2], base + STEP, xb);
+    score_rows(base, xa);
+    if (second) {
+      if (base + 2 * STEP < n_rows) load_rows(Kp, p.ks[2], base + 2 * STEP, xa);
+      score_rows(base + STEP, xb);
+    }
   }
   __syncthreads();
+  load_rows(Vp, p.vs[2], 0, xa);  // first V rows, in flight during pass 2
 
   // ---- pass 2: per-head max, exponentials, sums --------------------------------
   float m[G], l[G];
@@ -223,29 +247,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
-  for (int base = 0; base < n_rows; base += RSTEP * U) {
-    u32x4_t vx[U];
+  auto pv_rows = [&](int base, const u32x4_t (&vx)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int rl = base + u * RSTEP + wave * RPW + rr;
-      const int kv = kb_of(tile_of(rl)) * FA_BLOCK + rl % FA_BLOCK;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (rl < n_rows && kv < p.Skv) x = *(const u32x4_t*)(Vp + (long long)kv * p.vs[2] + 8 * sub);
-      vx[u] = x;
-    }
+      const int rl = base + u * RSTEP + my_row;
+      float vf[8];
+      unpack8(vx[u], vf);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rl = base + u * RSTEP + wave * RPW + rr;
-      if (rl < n_rows) {
-        float vf[8];
-        unpack8(vx[u], vf);
+      for (int g = 0; g < G; ++g) {
+        const float pg = sc[g][rl];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pg = sc[g][rl];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pg, vf[j], o[g][j]);
-        }
+        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pg, vf[j], o[g][j]);
       }
+    }
+  };
+  for (int base = 0; base < n_rows; base += 2 * STEP) {
+    const bool second = base + STEP < n_rows;
+    if (second) load_rows(Vp, p.vs[2], base + STEP, xb);
+    pv_rows(base, xa);
+    if (second) {
+      if (base + 2 * STEP < n_rows) load_rows(Vp, p.vs[2], base + 2 * STEP, xa);
+      pv_rows(base + STEP, xb);
     }
   }
   // sum over the row groups of the wave, then over waves
@@ -274,29 +296,57 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   }
 }
 
+// One 256-thread workgroup per (b, query head).  The splits are shared out
+// over 256 / D groups of D threads (thread = one output dim), each group
+// walking every (256 / D)-th split, so several partial rows are read at once.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(DecodeParams P) {
+  constexpr int NG = kDecThreads / D;
   const FwdParams& p = P.f;
-  const int bh = blockIdx.x, d = threadIdx.x;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = tid % D, grp = tid / D;
   const int b = bh / p.Hq, hq = bh % p.Hq;
   const float* lse = P.ws_lse + (long long)bh * P.splits;
+  const float* ws = P.ws_o + (long long)bh * P.splits * D;
+  __shared__ float red[kDecWaves];
+  __shared__ float part[2][NG][D];
+
   float m = -INFINITY;
-  for (int s = 0; s < P.splits; ++s) m = fmaxf(m, lse[s]);
+  for (int s = tid; s < P.splits; s += kDecThreads) m = fmaxf(m, lse[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, red[w]);
+
   float acc = 0.0f, tot = 0.0f;
   if (m > -INFINITY) {
-    for (int s = 0; s < P.splits; ++s) {
+#pragma unroll 4
+    for (int s = grp; s < P.splits; s += NG) {
       const float ls = lse[s];
-      if (ls == -INFINITY) continue;
+      if (ls == -INFINITY) continue;  // empty split: its output row was never written
       const float w = __builtin_amdgcn_exp2f(ls - m);
       tot += w;
-      acc = fmaf(w, P.ws_o[((long long)bh * P.splits + s) * D + d], acc);
+      acc = fmaf(w, ws[(long long)s * D + d], acc);
     }
   }
-  const float out = tot > 0.0f ? acc / tot : 0.0f;
-  uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1];
-  Op[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
-  if (p.lse != nullptr && d == 0)
-    p.lse[(long long)b * p.Hq + hq] = tot > 0.0f ? (m + __log2f(tot)) * kLn2 : -INFINITY;
+  part[0][grp][d] = acc;
+  part[1][grp][d] = tot;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      acc += part[0][g][d];
+      tot += part[1][g][d];
+    }
+    const float out = tot > 0.0f ? acc / tot : 0.0f;
+    uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1];
+    Op[d] = __builtin_bit_cast(uint16_t, (__bf16)out);
+    if (p.lse != nullptr && d == 0)
+      p.lse[(long long)b * p.Hq + hq] = tot > 0.0f ? (m + __log2f(tot)) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D, int G>
@@ -307,7 +357,7 @@ struct LaunchDecode {
   void operator()() {
     dim3 grid(P.splits, P.f.Hkv, P.f.B);
     hipLaunchKernelGGL((decode_partial_kernel<D, G, Score>), grid, dim3(kDecThreads), 0, stream, P);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(P.f.B * P.f.Hq), dim3(D), 0, stream, P);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(P.f.B * P.f.Hq), dim3(kDecThreads), 0, stream, P);
   }
 };
 
