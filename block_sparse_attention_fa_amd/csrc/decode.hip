@@ -103,7 +103,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   // tiles instead of addresses a power-of-two stride apart.
   const int n_tiles = T > split ? (T - split + P.splits - 1) / P.splits : 0;
   const long long ws_row0 = ((long long)b * p.Hq + (long long)hkv * G) * P.splits + split;
-  if (n_tiles == 0) {
+  if (n_tiles == 0) {  // empty chunk: LSE -inf and a zero row, so the merge needs no branch
+    for (int i = tid; i < G * D; i += kDecThreads)
+      P.ws_o[(ws_row0 + (long long)(i / D) * P.splits) * D + i % D] = 0.0f;
     if (tid < G) P.ws_lse[ws_row0 + (long long)tid * P.splits] = -INFINITY;
     return;
   }
@@ -323,11 +325,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(DecodeParams 
 
   float acc = 0.0f, tot = 0.0f;
   if (m > -INFINITY) {
-#pragma unroll 4
+    // every split wrote its row (zeros for an empty one), so the loads are
+    // independent of the weights and can all be in flight together
+#pragma unroll 8
     for (int s = grp; s < P.splits; s += NG) {
       const float ls = lse[s];
-      if (ls == -INFINITY) continue;  // empty split: its output row was never written
-      const float w = __builtin_amdgcn_exp2f(ls - m);
+      const float w = ls == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ls - m);
       tot += w;
       acc = fmaf(w, ws[(long long)s * D + d], acc);
     }
