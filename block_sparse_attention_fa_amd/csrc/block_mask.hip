@@ -3,10 +3,12 @@
 // Generating Optimized Attention Kernels", §4.1-4.2).
 //
 // One workgroup per BlockMask row (b', h', query tile).  Each wave classifies
-// whole 128x128 tiles: its 64 lanes each own up to two key columns of the
-// tile and walk the tile's in-range query rows, evaluating the mask_mod per
-// position; a wave vote gives "any position attends" / "every position
-// attends".  A tile is empty when none attends, full when all do, partial
+// whole 128x128 tiles.  Where the mask's structure decides the class exactly
+// (linear masks from the tile's corners, documents from the id ranges on each
+// side, and/or of decided parts) that answer is taken; otherwise its 64 lanes
+// each own up to two key columns of the tile and walk the tile's in-range
+// query rows, evaluating the mask_mod per position, and a wave vote gives
+// "any position attends" / "every position attends".  A tile is empty when none attends, full when all do, partial
 // otherwise.  Wave 0 then appends the tile ids of each class, in ascending
 // order, with a ballot + popcount prefix, so every list is written in order
 // without atomics.  All integer work: the result is bit-exact by construction.
@@ -20,13 +22,15 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 256;  // tiles classified per pass (kChunk / kWaves per wave)
 
-enum : int { kEmpty = 0, kPartial = 1, kFull = 2 };
+enum : int { kEmpty = kTileEmpty, kPartial = kTilePartial, kFull = kTileFull };
 
 template <class Mask>
 __device__ __forceinline__ int classify_tile(const BuildParams& p, int b, int h, int q0, int qn,
                                              int kb, int lane) {
   const int k0 = kb * kTile;
   const int kn = min(kTile, p.Skv - k0);
+  const int c = Mask::classify(p.mask, b, h, q0, q0 + qn - 1, k0, k0 + kn - 1, lane);
+  if (c != kTileUnknown) return c;
   const bool c0 = lane < kn;
   const bool c1 = lane + 64 < kn;
   bool any = false, all = true;

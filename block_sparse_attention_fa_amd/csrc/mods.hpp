@@ -17,6 +17,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "fa_internal.hpp"
@@ -32,7 +33,34 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 
 // ---------------------------------------------------------------------------
 // mask_mods
+//
+// classify(p, b, h, q0, q1, k0, k1, lane) gives the exact class of the
+// in-range rectangle [q0, q1] x [k0, k1] (inclusive) when the mask's structure
+// decides it, and kTileUnknown otherwise (the BlockMask builder then votes
+// position by position).  Every lane of a wave calls it with the same
+// arguments; the value is the same in every lane.
 // ---------------------------------------------------------------------------
+
+enum : int { kTileEmpty = 0, kTilePartial = 1, kTileFull = 2, kTileUnknown = 3 };
+
+// Class of a mask that attends exactly where an integer quantity x >= 0, x
+// taking every integer value between its minimum and maximum over the tile.
+__device__ __forceinline__ int classify_threshold(long long xmin, long long xmax) {
+  if (xmin >= 0) return kTileFull;
+  if (xmax < 0) return kTileEmpty;
+  return kTilePartial;
+}
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+  return x;
+}
 
 struct MaskNone {
   static constexpr bool kBatchDependent = false;
@@ -43,6 +71,9 @@ struct MaskNone {
   struct Tile {};
   static __device__ __forceinline__ Tile tile(const Row&, int) { return {}; }
   static __device__ __forceinline__ bool keep(const Tile&, int) { return true; }
+  static __device__ __forceinline__ int classify(const MaskParams&, int, int, int, int, int, int, int) {
+    return kTileFull;
+  }
 };
 
 // Concepts "mask_mod": causal, q >= kv.
@@ -58,6 +89,9 @@ struct MaskCausal {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.q - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr <= t.dq; }
+  static __device__ __forceinline__ int classify(const MaskParams&, int, int, int q0, int q1, int k0, int k1, int) {
+    return classify_threshold((long long)q0 - k1, (long long)q1 - k0);  // x = q - kv
+  }
 };
 
 // The window term of Concepts "Composing masks": q - kv <= window.
@@ -75,6 +109,9 @@ struct MaskWindow {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.lo - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr >= t.lo; }
+  static __device__ __forceinline__ int classify(const MaskParams& p, int, int, int q0, int q1, int k0, int k1, int) {
+    return classify_threshold((long long)k0 - q1 + p.window, (long long)k1 - q0 + p.window);  // x = kv - q + window
+  }
 };
 
 // Talk summary (variant list) / paper review §5.3: same document only.
@@ -95,6 +132,26 @@ struct MaskDocument {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.doc + kvb, r.dq}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return t.doc[cr] == t.dq; }
+  // One document on each side decides the tile; so do disjoint id ranges.
+  static __device__ int classify(const MaskParams& p, int b, int, int q0, int q1, int k0, int k1, int lane) {
+    const int* d = p.doc + (long long)b * p.doc_stride_b;
+    int qmin = INT_MAX, qmax = INT_MIN, kmin = INT_MAX, kmax = INT_MIN;
+    for (int i = q0 + lane; i <= q1; i += 64) {
+      qmin = min(qmin, d[i]);
+      qmax = max(qmax, d[i]);
+    }
+    for (int i = k0 + lane; i <= k1; i += 64) {
+      kmin = min(kmin, d[i]);
+      kmax = max(kmax, d[i]);
+    }
+    qmin = wave_min(qmin);
+    qmax = wave_max(qmax);
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (qmax < kmin || kmax < qmin) return kTileEmpty;
+    if (qmin == qmax && kmin == kmax) return kTileFull;  // (ids equal: the ranges overlap)
+    return kTileUnknown;
+  }
 };
 
 // The prefix term of paper review §4.4: keys before prefix_len are visible to all.
@@ -110,6 +167,9 @@ struct MaskPrefix {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
+  static __device__ __forceinline__ int classify(const MaskParams& p, int, int, int, int, int k0, int k1, int) {
+    return classify_threshold((long long)p.prefix_len - 1 - k1, (long long)p.prefix_len - 1 - k0);
+  }
 };
 
 // Valid prefix of a KV cache: kv < kv_len[b].
@@ -125,6 +185,10 @@ struct MaskKvLen {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
+  static __device__ __forceinline__ int classify(const MaskParams& p, int b, int, int, int, int k0, int k1, int) {
+    const int n = p.kv_len[b];
+    return classify_threshold((long long)n - 1 - k1, (long long)n - 1 - k0);
+  }
 };
 
 // Logical fusion (paper review §4.4; Concepts "Composing masks").
@@ -145,6 +209,15 @@ struct MaskAnd {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) && B::keep(t.b, cr); }
+  static __device__ int classify(const MaskParams& p, int b, int h, int q0, int q1, int k0, int k1, int lane) {
+    const int ca = A::classify(p, b, h, q0, q1, k0, k1, lane);
+    if (ca == kTileEmpty) return kTileEmpty;
+    const int cb = B::classify(p, b, h, q0, q1, k0, k1, lane);
+    if (cb == kTileEmpty) return kTileEmpty;
+    if (ca == kTileFull) return cb;
+    if (cb == kTileFull) return ca;
+    return kTileUnknown;  // partial AND partial can be anything
+  }
 };
 
 template <class A, class B>
@@ -164,6 +237,15 @@ struct MaskOr {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) || B::keep(t.b, cr); }
+  static __device__ int classify(const MaskParams& p, int b, int h, int q0, int q1, int k0, int k1, int lane) {
+    const int ca = A::classify(p, b, h, q0, q1, k0, k1, lane);
+    if (ca == kTileFull) return kTileFull;
+    const int cb = B::classify(p, b, h, q0, q1, k0, k1, lane);
+    if (cb == kTileFull) return kTileFull;
+    if (ca == kTileEmpty) return cb;
+    if (cb == kTileEmpty) return ca;
+    return kTileUnknown;  // partial OR partial can be anything
+  }
 };
 
 using MaskSlidingCausal = MaskAnd<MaskCausal, MaskWindow>;
