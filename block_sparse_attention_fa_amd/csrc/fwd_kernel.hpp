@@ -149,6 +149,10 @@ void fwd_kernel(FwdParams p) {
   constexpr int NK = 2, NV = 3;               // ring depths: K of j+1 / j+2, V of j-1 / j / j+1
   __shared__ __align__(16) uint16_t k_lds[NK][HB * D];
   __shared__ __align__(16) uint16_t v_lds[NV][HB * D];
+  // Bias tiles [128 query rows x 64 keys] of steps j and j+1 (only for the
+  // staged bias): row r holds its 8 16-byte chunks c at slot c ^ (r % 8).
+  constexpr bool BL = Score::kStagesBias;
+  __shared__ __align__(16) uint16_t b_lds[BL ? 2 : 1][BL ? kBM * HB : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,6 +244,37 @@ void fwd_kernel(FwdParams p) {
   auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
   auto issue_k = [&](int j) { issue_one(Kp, ksb, k_lds[j % NK], kchunk, k_voff, kv0_of(j)); };
   auto issue_v = [&](int j) { issue_one(Vp, vsb, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
+  // Bias tile of sub-tile j -> b_lds[j % 2]: wave w issues slots 64 (4i + w) + lane
+  // (i < 4), i.e. row 32 i + 8 w + lane / 8, stored slot lane % 8 holding chunk
+  // bc = (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
+  const int b_row = 8 * wave + (lane >> 3);  // + 32 i
+  const int bc = (lane & 7) ^ ((lane >> 3) & 7);
+  const char* Bbh = nullptr;
+  long long bsb = 0;  // bias row stride in bytes
+  uint32_t b_voff = 0;
+  if constexpr (BL) {
+    Bbh = (const char*)(p.score.bias + (long long)b * p.score.bs0 + (long long)hq * p.score.bs1);
+    bsb = 2 * p.score.bs2;
+    b_voff = (uint32_t)(b_row * bsb + 16 * bc);
+  }
+  auto issue_b = [&](int j) {
+    if constexpr (BL) {
+      const int kv0 = kv0_of(j);
+      const uint32_t base = lds_address(b_lds[j % 2]) + 16 * 64 * wave;
+      if (q0 + kBM <= p.Sq && kv0 + HB <= p.Skv) {
+        const char* g0 = Bbh + (long long)q0 * bsb + 2 * kv0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16s(b_voff, g0 + 32 * i * bsb, base + 16 * 64 * 4 * i);
+      } else {  // ragged: clamp rows to Sq-1 and chunks to the last one of the row
+        const int kc = min(kv0 + 8 * bc, p.Skv - 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = min(q0 + 32 * i + b_row, p.Sq - 1);
+          dma16(Bbh + (long long)q * bsb + 2 * kc, base + 16 * 64 * 4 * i);
+        }
+      }
+    }
+  };
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
   auto v_off = [](int r, int chunk) { return r * D + ((chunk ^ v_swizzle<D>(r)) * 8); };
 
@@ -326,10 +361,11 @@ void fwd_kernel(FwdParams p) {
       for (int i = tid; i < HB * D / 8; i += kFwdThreads) vz[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
     issue_k(0);
+    issue_b(0);
     if (J > 1) issue_k(1);
     issue_v(0);
     if (J > 1)
-      wait_vmcnt<2 * NI>();  // K(0) landed (K(1), V(0) may be in flight)
+      wait_vmcnt<2 * NI>();  // K(0) (and the bias of 0) landed (K(1), V(0) may be in flight)
     else
       wait_vmcnt<NI>();
     wait_lds_reads();
@@ -359,7 +395,10 @@ void fwd_kernel(FwdParams p) {
         loaded(win);
       }
       if (j + 2 < J) issue_k(j + 2);
-      if (j + 1 < J) issue_v(j + 1);
+      if (j + 1 < J) {
+        issue_b(j + 1);  // before V(j+1), so "only V in flight" also covers it
+        issue_v(j + 1);
+      }
 
       const int kvt0 = kb_of(t) * kBN + HB * H;
       const bool partial = t < n_part;
@@ -374,12 +413,30 @@ void fwd_kernel(FwdParams p) {
       const auto st = Score::tile(srow, kvb, m_ref);
       const int lim = ragged ? p.Skv - kvb : HB;  // key kvb + cr exists iff cr < lim
       float ymax = -INFINITY;
+      // staged bias: chunk g (keys 8g..8g+7) of this lane's row, half hh
+      uint32_t bias2[8][2];
+      if constexpr (BL) {
+        const int br = 32 * wave + lq;
+        const uint32_t rowa = lds_address(b_lds[j % 2]) + 128 * br + 8 * hh;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const uint64_t w = *(const __attribute__((address_space(3))) uint64_t*)(uintptr_t)(rowa + 16 * (g ^ (br & 7)));
+          bias2[g][0] = (uint32_t)w;
+          bias2[g][1] = (uint32_t)(w >> 32);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int mt = e >> 4, r = e & 15;
         const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-        // functors that read memory get an in-bounds key on the ragged tile
-        const float y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
+        float y;
+        if constexpr (BL) {  // element (mt, r) is component r % 4 of chunk 4 mt + r / 4
+          const uint32_t w = bias2[4 * mt + (r >> 2)][(r >> 1) & 1];
+          y = Score::apply_bits(st, s_cur[mt][r], (r & 1) ? (w >> 16) : (w & 0xffffu));
+        } else {
+          // functors that read memory get an in-bounds key on the ragged tile
+          y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
+        }
         s_cur[mt][r] = y;
         ymax = fmaxf(ymax, y);
         if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
@@ -387,12 +444,27 @@ void fwd_kernel(FwdParams p) {
       if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
         const auto mtl = Mask::tile(mrow, kvb);
         ymax = -INFINITY;
+        // A mask that reads memory (document ids) is evaluated for every element
+        // first, in-bounds and without branches, so all its loads are in flight
+        // at once; the others are evaluated where needed.
+        bool mk[32];
+        if constexpr (Mask::kReadsMemory) {
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int mt = e >> 4, r = e & 15;
+            mk[e] = Mask::keep(mtl, min(32 * mt + 8 * (r >> 2) + (r & 3), lim - 1));
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           const int mt = e >> 4, r = e & 15;
           const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
           bool keep = cr < lim;
-          if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+          if constexpr (Mask::kReadsMemory) {
+            keep = keep && (mk[e] || !partial);
+          } else {
+            if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+          }
           const float y = keep ? s_cur[mt][r] : -INFINITY;
           s_cur[mt][r] = y;
           ymax = fmaxf(ymax, y);
@@ -481,6 +553,16 @@ struct LaunchFwd {
   void operator()() {
     const int NQ = (p.Sq + kBM - 1) / kBM;
     const long long total = (long long)NQ * p.Hq * p.B;
+    if constexpr (std::is_same<Score, ScoreBias>::value) {
+      const ScoreParams& s = p.score;
+      const bool aligned = ((uintptr_t)s.bias % 16 == 0) && s.bs0 % 8 == 0 && s.bs1 % 8 == 0 &&
+                           s.bs2 % 8 == 0 && p.Skv % 8 == 0;
+      if (aligned) {
+        hipLaunchKernelGGL((fwd_kernel<D, Mask, ScoreBiasTiled>), dim3((unsigned)total), dim3(kFwdThreads), 0,
+                           stream, p);
+        return;
+      }
+    }
     hipLaunchKernelGGL((fwd_kernel<D, Mask, Score>), dim3((unsigned)total), dim3(kFwdThreads), 0,
                        stream, p);
   }

@@ -64,6 +64,7 @@ __device__ __forceinline__ int wave_max(int x) {
 
 struct MaskNone {
   static constexpr bool kBatchDependent = false;
+  static constexpr bool kReadsMemory = false;
   struct Row {
     __device__ __forceinline__ bool operator()(int) const { return true; }
   };
@@ -79,6 +80,7 @@ struct MaskNone {
 // Concepts "mask_mod": causal, q >= kv.
 struct MaskCausal {
   static constexpr bool kBatchDependent = false;
+  static constexpr bool kReadsMemory = false;
   struct Row {
     int q;
     __device__ __forceinline__ bool operator()(int kv) const { return q >= kv; }
@@ -97,6 +99,7 @@ struct MaskCausal {
 // The window term of Concepts "Composing masks": q - kv <= window.
 struct MaskWindow {
   static constexpr bool kBatchDependent = false;
+  static constexpr bool kReadsMemory = false;
   struct Row {
     int lo;  // smallest kv with q - kv <= window
     __device__ __forceinline__ bool operator()(int kv) const { return kv >= lo; }
@@ -117,6 +120,7 @@ struct MaskWindow {
 // Talk summary (variant list) / paper review §5.3: same document only.
 struct MaskDocument {
   static constexpr bool kBatchDependent = true;
+  static constexpr bool kReadsMemory = true;
   struct Row {
     const int* doc;
     int dq;
@@ -157,6 +161,7 @@ struct MaskDocument {
 // The prefix term of paper review §4.4: keys before prefix_len are visible to all.
 struct MaskPrefix {
   static constexpr bool kBatchDependent = false;
+  static constexpr bool kReadsMemory = false;
   struct Row {
     int n;
     __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
@@ -175,6 +180,7 @@ struct MaskPrefix {
 // Valid prefix of a KV cache: kv < kv_len[b].
 struct MaskKvLen {
   static constexpr bool kBatchDependent = true;
+  static constexpr bool kReadsMemory = false;
   struct Row {
     int n;
     __device__ __forceinline__ bool operator()(int kv) const { return kv < n; }
@@ -195,6 +201,7 @@ struct MaskKvLen {
 template <class A, class B>
 struct MaskAnd {
   static constexpr bool kBatchDependent = A::kBatchDependent || B::kBatchDependent;
+  static constexpr bool kReadsMemory = A::kReadsMemory || B::kReadsMemory;
   struct Row {
     typename A::Row a;
     typename B::Row b;
@@ -223,6 +230,7 @@ struct MaskAnd {
 template <class A, class B>
 struct MaskOr {
   static constexpr bool kBatchDependent = A::kBatchDependent || B::kBatchDependent;
+  static constexpr bool kReadsMemory = A::kReadsMemory || B::kReadsMemory;
   struct Row {
     typename A::Row a;
     typename B::Row b;
@@ -280,6 +288,7 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 
 struct ScoreNone {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kStagesBias = false;
   struct Row {
     float c;
   };
@@ -295,6 +304,7 @@ struct ScoreNone {
 // Concepts "score_mod": s + slope[h] * (kv - q).
 struct ScoreAlibi {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kStagesBias = false;
   struct Row {
     float c;    // scale * log2e
     float sl;   // slope[h] * log2e
@@ -323,6 +333,7 @@ struct ScoreAlibi {
 // reciprocal; the error this adds is measured against fp64 tanh in the tests.
 struct ScoreSoftcap {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kStagesBias = false;
   struct Row {
     float k;     // 2 * scale / cap * log2e
     float c2;    // cap * log2e
@@ -349,6 +360,7 @@ struct ScoreSoftcap {
 // Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
 struct ScoreRelPos {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kStagesBias = false;
   struct Row {
     float c;
     int q;
@@ -371,6 +383,7 @@ struct ScoreRelPos {
 // Dynamic-bias feature request (attention-gym issue 123): s + bias[b,h,q,kv].
 struct ScoreBias {
   static constexpr bool kReadsMemory = true;
+  static constexpr bool kStagesBias = false;
   struct Row {
     float c;
     const uint16_t* row;  // bias[b, h, q, :]
@@ -390,6 +403,19 @@ struct ScoreBias {
   }
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(kLog2e, bf16_bits_to_float(t.row[cr]), t.add));
+  }
+};
+
+// The dynamic bias with the forward staging each step's [128 query x 64 key]
+// bias tile in LDS (coalesced 16-byte loads) instead of every lane reading its
+// own row element by element.  Same arithmetic as ScoreBias; used when the
+// bias layout is 16-byte aligned (base, row strides and Skv multiples of 8
+// elements).
+struct ScoreBiasTiled : ScoreBias {
+  static constexpr bool kStagesBias = true;
+  // x2 - m_ref for raw score s and a bias value b (bf16 bits).
+  static __device__ __forceinline__ float apply_bits(const Tile& t, float s, uint32_t b) {
+    return fmaf(s, t.c, fmaf(kLog2e, bf16_bits_to_float(b), t.add));
   }
 };
 

@@ -80,6 +80,16 @@ def test_explicit_alibi_slopes_and_broadcast_bias():
     run_case(34, "causal", "bias", 2, 4, 2, 270, 270, 64, bias_broadcast=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,Sq,Skv", [("causal", 392, 392), ("none", 264, 392), ("document_causal", 256, 256),
+                                         ("sliding_window", 392, 264)])
+def test_bias_staged_through_lds(mask, Sq, Skv, D):
+    # Skv a multiple of 8 and 16-byte aligned rows: the bias tile goes through
+    # LDS (ragged query and key tiles included); the same result as the oracle.
+    run_case(40 + D, mask, "bias", 2, 2, 1, Sq, Skv, D)
+    run_case(41 + D, mask, "bias", 1, 2, 2, Sq, Skv, D, bias_broadcast=True)
+
+
 def test_fully_masked_rows_are_zero_with_neg_inf_lse():
     # kv_len = 0 for a batch row: every row of it is empty
     import torch
