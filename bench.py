@@ -222,7 +222,7 @@ def main():
         sc = fa.ScoreMod("softcap", softcap=DEC["cap"])
         ws = torch.empty(fa.fa_decode_workspace_size(qdt, kct, vct, bmd, sc) // 4 + 1,
                          dtype=torch.float32, device=dev)
-        for _ in range(3):
+        for _ in range(max(10, args.warmup)):
             fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws)
         torch.cuda.synchronize()
         e0.record(stream)
