@@ -300,9 +300,11 @@ void fwd_kernel(FwdParams p) {
   // then only raised when a score exceeds it by more than kRescaleSlack.  Scores
   // are produced relative to it (y = x2 - m_run), so exp2(y) needs no subtraction.
   float m_run = -INFINITY;
-  float l_run = 0.0f;  // this lane's half of the row sum
+  // This lane's half of the row sum, in four fp32 partial sums of the
+  // exponentials (plain adds: on gfx950 a v_dot2 instruction cannot run while
+  // an MFMA is in flight, a v_add can).
+  float l_run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Per-lane element offsets of the MFMA operands inside a K or V stage.  The
   // swizzle only depends on the row bits that belong to the lane (32-row
@@ -480,7 +482,8 @@ void fwd_kernel(FwdParams p) {
         const float m_new = fmaxf(m_run, m_ref + ymax);
         const float shift = m_new == -INFINITY ? 0.0f : m_ref - m_new;
         const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l_run[k] *= alpha;
 #pragma unroll
         for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
 #pragma unroll
@@ -497,9 +500,11 @@ void fwd_kernel(FwdParams p) {
         bf16x2_t pk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          pk[k][0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k]);
-          pk[k][1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k + 1]);
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, l_run, false);
+          const float e0 = __builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k]);
+          const float e1 = __builtin_amdgcn_exp2f(s_cur[mt][h8 + 2 * k + 1]);
+          pk[k][0] = (__bf16)e0;
+          pk[k][1] = (__bf16)e1;
+          l_run[k] += e0 + e1;
           if (4 * g + k < 2 * KS) qk_mfma(s_nxt, 4 * g + k);  // D=64 has 8 QK MFMAs
         }
         p_prev[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
@@ -521,7 +526,8 @@ void fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------------
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float lh = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
+  const float l = lh + __shfl_xor(lh, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (q_ok) {
     uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)myq * p.os[2];
