@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -222,7 +222,7 @@ def main():
         sc = fa.ScoreMod("softcap", softcap=DEC["cap"])
         ws = torch.empty(fa.fa_decode_workspace_size(qdt, kct, vct, bmd, sc) // 4 + 1,
                          dtype=torch.float32, device=dev)
-        for _ in range(max(10, args.warmup)):
+        for _ in range(max(30, args.warmup)):  # settle clocks after the forward leg
             fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws)
         torch.cuda.synchronize()
         e0.record(stream)
