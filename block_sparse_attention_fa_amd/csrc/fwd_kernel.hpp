@@ -443,6 +443,10 @@ void fwd_kernel(FwdParams p) {
         ymax = fmaxf(ymax, y);
         if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
       }
+      // Keep the row max of the unmasked scores here, beside the PV MFMAs: left
+      // alone, the compiler moves it (and a copy of every score register) past
+      // the masked-pass branch, where no MFMA is in flight to cover it.
+      asm volatile("" : "+v"(ymax));
       if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
         const auto mtl = Mask::tile(mrow, kvb);
         ymax = -INFINITY;
