@@ -225,7 +225,26 @@ def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, devi
     return bm
 
 
+def _check_tensors(q, k, v, out, lse):
+    """What the C ABI cannot see from pointers and strides: dtypes, devices, and
+    the dims it takes from q and k alone (k's B and D, v's shape, out, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise FAError(FA_ERR_SHAPE, f"{name} must be a 4-d torch.bfloat16 tensor")
+    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3] or tuple(v.shape) != tuple(k.shape):
+        raise FAError(FA_ERR_SHAPE, f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    if tuple(out.shape) != tuple(q.shape):
+        raise FAError(FA_ERR_SHAPE, f"out has shape {tuple(out.shape)}, q has {tuple(q.shape)}")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise FAError(FA_ERR_SHAPE, "lse must be a contiguous torch.float32 [B, Hq, Sq] tensor")
+    if not all(t.is_cuda for t in (q, k, v, out) + ((lse,) if lse is not None else ())):
+        raise FAError(FA_ERR_SHAPE, "every tensor must be on the GPU")
+
+
 def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits):
+    _check_tensors(q, k, v, out, lse)
     a = AttnArgs()
     a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None

@@ -152,3 +152,27 @@ def test_decode_validation_and_workspace_size():
     assert _status(a, decode=True) == fa.FA_ERR_UNSUPPORTED
     a = _args(Sq=1, Skv=512)
     assert fa.lib().fa_decode(ctypes.byref(a), None, 0, None) == fa.FA_ERR_WORKSPACE
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks what the C ABI cannot see (it takes B, Hq, Sq, D from q
+    and Hkv, Skv from k, and gets out/lse as bare pointers) before any call."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((2, 4, 64, 64), dtype=bf)
+    k = torch.zeros((2, 2, 96, 64), dtype=bf)
+    cases = [
+        dict(q=q.float(), k=k, v=k),                                  # dtype
+        dict(q=q[0], k=k, v=k),                                       # rank
+        dict(q=q, k=torch.zeros((1, 2, 96, 64), dtype=bf), v=k),     # batch of k
+        dict(q=q, k=torch.zeros((2, 2, 96, 128), dtype=bf), v=k),    # head dim of k
+        dict(q=q, k=k, v=torch.zeros((2, 2, 80, 64), dtype=bf)),     # v differs from k
+        dict(q=q, k=k, v=k, out=torch.zeros((2, 4, 63, 64), dtype=bf)),
+        dict(q=q, k=k, v=k, lse=torch.zeros((2, 4, 64), dtype=torch.float64)),
+        dict(q=q, k=k, v=k, lse=torch.zeros((2, 64, 4), dtype=torch.float32).transpose(1, 2)),
+        dict(q=q, k=k, v=k),                                          # right shapes, host memory
+    ]
+    for c in cases:
+        with pytest.raises(fa.FAError) as e:
+            fa.fa_forward(c["q"], c["k"], c["v"], out=c.get("out"), lse=c.get("lse"))
+        assert e.value.status == fa.FA_ERR_SHAPE, c

@@ -76,3 +76,32 @@ def test_decode_workspace_errors():
     with pytest.raises(fa.FAError) as e:
         fa.fa_decode(q3, kv, kv)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+def test_empty_sequence_strided_cache_and_scale():
+    """A sequence with kv_len = 0 (every split empty: O = 0 and LSE = -inf), the
+    caches as [B,H,KV,D] views of [B,KV,H,D] buffers, and a scale other than 1/sqrt(D)."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, Hq, Hkv, KV, D, scale = 3, 8, 2, 1300, 128, 0.07
+    print(f"[case] decode empty sequence, strided caches, scale={scale}", flush=True)
+    q = gen.qkv(55, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(56, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([900, 0, 1300], dtype=np.int32)
+
+    def bshd_view(x):  # same values, stored as [B,KV,H,D]
+        return gen.to_torch_bf16(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+
+    kt, vt = bshd_view(k), bshd_view(v)
+    assert not kt.is_contiguous()
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    out = fa.fa_decode(gen.to_torch_bf16(q), kt, vt, block_mask=bm, score=fa.ScoreMod("softcap", softcap=50.0),
+                       scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    got = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    gl = lse.cpu().numpy()
+    O, L = fo.decode(q, k, v, lens, fo.softcap(50.0), scale=scale)
+    C.compare(got, O, "decode strided")
+    C.compare_lse(gl[..., 0], L[..., 0], "decode strided")
+    assert np.all(got[1] == 0.0) and np.all(np.isneginf(gl[1]))

@@ -90,6 +90,32 @@ def test_bias_staged_through_lds(mask, Sq, Skv, D):
     run_case(41 + D, mask, "bias", 1, 2, 2, Sq, Skv, D, bias_broadcast=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_strided_views_and_custom_scale(D):
+    """Q, K, V and O as [B,H,S,D] views of [B,S,H,D] buffers (the layout a fused
+    projection produces), with a softmax scale other than 1/sqrt(D)."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, Hq, Hkv, S, scale = 2, 4, 2, 300, 0.05
+    print(f"[case] strided views D={D} scale={scale}", flush=True)
+    q, k, v = gen.qkv(61, B, Hq, Hkv, S, S, D)
+
+    def bshd_view(x):  # same values, stored as [B,S,H,D]
+        return gen.to_torch_bf16(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+
+    qt, kt, vt = bshd_view(q), bshd_view(k), bshd_view(v)
+    assert not qt.is_contiguous() and qt.stride(2) == Hq * D
+    out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, 1, S, S)
+    fa.fa_forward(qt, kt, vt, block_mask=bm, score=fa.ScoreMod("alibi"), scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    got = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    O, L = fo.attention(q, k, v, fo.causal(), fo.alibi(fo.default_alibi_slopes(Hq)), scale=scale)
+    C.compare(got, O, "strided views")
+    C.compare_lse(lse.cpu().numpy(), L, "strided views")
+
+
 def test_fully_masked_rows_are_zero_with_neg_inf_lse():
     # kv_len = 0 for a batch row: every row of it is empty
     import torch
