@@ -8,7 +8,8 @@ split-KV decode (B=32, Hq=32, Hkv=8, D=128, KV cache 32768 with valid lengths
 uniform in [4096, 32768], softcap 50) is timed in the same run and reported as
 HBM GB/s.  Inputs are resident in HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 30]   (at least 30 untimed steps)
+    python bench.py --ablation                              (block-skipping ablation, sparsity sweep)
 """
 
 import argparse
@@ -92,15 +93,80 @@ def cpu_baseline(q, k, v, seconds):
                       f"host cpu_count={os.cpu_count()}"}
 
 
+def run_ablation(steps):
+    """Block-skipping ablation and a sparsity sweep on the causal + ALiBi forward
+    workload (B4 H16 S8192 D128): what skipping empty tiles and running full
+    tiles without the mask_mod save, and how the time follows the fraction of
+    non-empty tiles (sliding-window widths).  Each entry is the best of three
+    timed runs of `steps` calls.  Prints one JSON line."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    from block_sparse_attention_fa_amd import inputs as gen
+    fa.lib()
+    B, H, S, D = FWD["B"], FWD["H"], FWD["S"], FWD["D"]
+    q, k, v = gen.qkv(FWD["workload_id"], B, H, H, S, S, D)
+    qt, kt, vt = (gen.to_torch_bf16(x) for x in (q, k, v))
+    out = torch.empty_like(qt)
+    score = fa.ScoreMod("alibi")
+
+    def time_fwd(bm):
+        for _ in range(3):
+            fa.fa_forward(qt, kt, vt, block_mask=bm, score=score, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fa.fa_forward(qt, kt, vt, block_mask=bm, score=score, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def entry(bm, n_att):
+        ms = min(time_fwd(bm) for _ in range(3))
+        cls = bm.classes() if bm.separate_full else None
+        listed = int(bm.kv_num_blocks.sum().item()) + (int(bm.full_kv_num_blocks.sum().item()) if bm.separate_full else 0)
+        e = {"ms": round(ms, 4), "attended_tflops": round(4.0 * D * n_att / (ms * 1e-3) / 1e12, 2),
+             "tiles_visited": listed,
+             "executed_tile_tflops": round(4.0 * D * 128 * 128 * listed * B * H / (ms * 1e-3) / 1e12, 2)}
+        if cls is not None:
+            e["tiles_partial"], e["tiles_full"] = int((cls == 1).sum()), int((cls == 2).sum())
+        return e
+
+    n_causal = B * H * S * (S + 1) // 2
+    causal = fa.MaskMod("causal")
+    warm = fa.fa_build_block_mask(causal, 1, 1, S, S)
+    for _ in range(30):  # clocks and caches settle before the first timed mode
+        fa.fa_forward(qt, kt, vt, block_mask=warm, score=score, out=out)
+    modes = {
+        "skip_empty__mask_on_partial_only": entry(fa.fa_build_block_mask(causal, 1, 1, S, S), n_causal),
+        "skip_empty__mask_on_every_tile": entry(fa.fa_build_block_mask(causal, 1, 1, S, S, separate_full=False),
+                                                n_causal),
+        "no_skipping__mask_on_every_tile": entry(
+            fa.fa_build_block_mask(causal, 1, 1, S, S, separate_full=False).list_every_tile(), n_causal),
+    }
+    sweep = []
+    for W in (256, 1024, 2048, 4096, S - 1):
+        bm = fa.fa_build_block_mask(fa.MaskMod("sliding_causal", window=W), 1, 1, S, S)
+        n_att = B * H * (W * (W + 1) // 2 + (S - W) * (W + 1))   # row q attends min(q, W) + 1 keys
+        e = entry(bm, n_att)
+        e["window"] = W
+        e["nonempty_tile_frac"] = round((e["tiles_partial"] + e["tiles_full"]) / float(bm.NQ * bm.NK), 4)
+        sweep.append(e)
+    print(json.dumps({"ablation": {"workload": FWD["name"], "steps": steps, "modes": modes,
+                                   "sliding_causal_window_sweep": sweep}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="only time the block-skipping ablation and the sliding-window sparsity sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain fp16->bf16 copies of MIB MiB each (reads MIB MiB, writes "
                          "MIB MiB): the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -123,6 +189,9 @@ def main():
         print(json.dumps({"copy_calibration": {"kernel": "fp16->bf16 elementwise copy", "launches": 5,
                                                "read_bytes_per_launch": 2 * n,
                                                "write_bytes_per_launch": 2 * n}}), flush=True)
+        return
+    if args.ablation:
+        run_ablation(args.steps)
         return
     from block_sparse_attention_fa_amd import fa
     from block_sparse_attention_fa_amd import inputs as gen
@@ -153,7 +222,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
+    # At least 30 untimed steps: the GPU needs about that many calls (tens of ms of
+    # continuous work) to reach its steady clock; with 3 the timed steps run
+    # about 10% slower than in steady operation.
+    fwd_settle = max(30, args.warmup)
+    for _ in range(fwd_settle):
         step()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -187,7 +260,7 @@ def main():
     result = {
         "metric": "fwd attended TFLOP/s & % bf16 MFMA peak; decode HBM GB/s (1 MI355X)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "warmup": fwd_settle, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": FWD["name"], "B": B, "H": H, "S": S, "D": D, "mask": "causal",
                    "score_mod": "alibi", "block": 128, "step": "fa_build_block_mask + fa_forward"},
@@ -222,7 +295,8 @@ def main():
         sc = fa.ScoreMod("softcap", softcap=DEC["cap"])
         ws = torch.empty(fa.fa_decode_workspace_size(qdt, kct, vct, bmd, sc) // 4 + 1,
                          dtype=torch.float32, device=dev)
-        for _ in range(max(30, args.warmup)):  # settle clocks after the forward leg
+        dec_settle = max(30, args.warmup)
+        for _ in range(dec_settle):  # settle clocks after the forward leg
             fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -236,6 +310,7 @@ def main():
         gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
         result["decode"] = {
             "workload": DEC["name"], "ms": round(dec_ms, 4), "GB/s": round(gbs, 1),
+            "untimed_calls": dec_settle, "timed_calls": args.decode_steps,
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dec_bytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -180,6 +180,19 @@ class BlockMask:
         c.separate_full = 1 if separate_full else 0
         c.mask = mask.desc()
 
+    def list_every_tile(self):
+        """Re-encode as "no block skipping": every tile of every row is listed as
+        partial (superset encoding), so the forward visits all of them and applies
+        the mask_mod everywhere, the way masking through a score_mod would.  Only
+        for measuring what block sparsity and mask-free full tiles save."""
+        import torch
+        self.kv_num_blocks.fill_(self.NK)
+        self.kv_indices.copy_(torch.arange(self.NK, dtype=torch.int32, device=self.kv_indices.device)
+                              .expand_as(self.kv_indices))
+        self.separate_full = False
+        self.c.separate_full = 0
+        return self
+
     def tensors(self):
         return {"kv_num_blocks": self.kv_num_blocks, "kv_indices": self.kv_indices,
                 "full_kv_num_blocks": self.full_kv_num_blocks, "full_kv_indices": self.full_kv_indices}

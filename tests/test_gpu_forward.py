@@ -66,6 +66,28 @@ def test_superset_encoding(mask):
     run_case(30, mask, "softcap", 2, 2, 2, 384, 384, 64, separate_full=False)
 
 
+@pytest.mark.parametrize("mask", ["causal", "document_causal", "kv_len"])
+def test_every_tile_listed_as_partial(mask):
+    """The "no block skipping" encoding (every tile listed, the mask_mod applied to
+    all of them) computes the same attention as the canonical BlockMask."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, H, S, D = 2, 2, 392, 128
+    print(f"[case] every tile listed, mask={mask}", flush=True)
+    q, k, v = gen.qkv(71, B, H, H, S, S, D)
+    spec = C.make_spec(71, mask, "alibi", B, H, S, S)
+    Bm = B if mask in BATCH_DEP else 1
+    bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, 1, S, S, separate_full=False).list_every_tile()
+    torch.cuda.synchronize()
+    assert int(bm.kv_num_blocks.min().item()) == bm.NK
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    out = fa.fa_forward(*(gen.to_torch_bf16(x) for x in (q, k, v)), block_mask=bm, score=C.gpu_score(spec), lse=lse)
+    torch.cuda.synchronize()
+    O, L = fo.attention(q, k, v, C.oracle_mask(spec), C.oracle_score(spec, H))
+    C.compare(gen.bf16_bits_to_f32(gen.from_torch_bf16(out)), O, f"every tile {mask}")
+    C.compare_lse(lse.cpu().numpy(), L, f"every tile {mask}")
+
+
 @pytest.mark.parametrize("score", ["none", "alibi", "bias"])
 def test_dense_without_blockmask(score):
     run_case(31, "none", score, 1, 4, 4, 250, 250, 128, dense=True)
