@@ -63,7 +63,7 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int D, int G, class Score>
+template <int D, int G, class Score, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
   constexpr int LPR = D / 8;          // lanes per K/V row (16 bytes each)
   constexpr int RPW = 64 / LPR;       // rows per wave per load
@@ -112,17 +112,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   const int n_rows = n_tiles * FA_BLOCK;
   // First key of each of this chunk's tiles and whether the tile is partial,
   // looked up once (the row loads below then depend on no global read).
+  // With a paged cache (paper review §4.5) the tile's rows come from the page
+  // the table gives for its logical block; the mods keep the logical key.
+  // (A template parameter, so the per-sequence-cache kernel carries none of it.)
   __shared__ int s_kv0[kMaxBps];
   __shared__ int s_part[kMaxBps];
+  __shared__ long long s_koff[kMaxBps], s_voff[kMaxBps];  // first row of the tile, elements from Kp / Vp
   if (tid < n_tiles) {
     const int t = split + tid * P.splits;
     const int kb = t < n_part ? part_idx[t] : (bm.dense ? t - n_part : full_idx[t - n_part]);
     s_kv0[tid] = kb * FA_BLOCK;
     s_part[tid] = t < n_part;
+    if constexpr (PAGED) {
+      const int pg = min(max(P.page_table[(long long)b * P.pt_stride + kb], 0), P.num_pages - 1);
+      s_koff[tid] = (long long)pg * p.ks[0];
+      s_voff[tid] = (long long)pg * p.vs[0];
+    }
   }
 
-  const uint16_t* Kp = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1];
-  const uint16_t* Vp = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1];
+  const uint16_t* Kp = p.k + (PAGED ? 0LL : (long long)b * p.ks[0]) + (long long)hkv * p.ks[1];
+  const uint16_t* Vp = p.v + (PAGED ? 0LL : (long long)b * p.vs[0]) + (long long)hkv * p.vs[1];
 
   // query slices (8 dims per lane) of the G heads
   float qf[G][8];
@@ -143,13 +152,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   constexpr int STEP = RSTEP * U;
   static_assert(FA_BLOCK % STEP == 0, "an iteration stays inside one tile");
   const int my_row = wave * RPW + rr;
-  auto load_rows = [&](const uint16_t* X, long long xs, int base, u32x4_t (&x)[U]) {
-    const int kv0 = s_kv0[base / FA_BLOCK] + base % FA_BLOCK + my_row;
+  auto load_rows = [&](const uint16_t* X, long long xs, bool v_rows, int base, u32x4_t (&x)[U]) {
+    const int t = base / FA_BLOCK, r0 = base % FA_BLOCK + my_row;
+    const int kv0 = s_kv0[t] + r0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kv = kv0 + u * RSTEP;
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (kv < p.Skv) v = *(const u32x4_t*)(X + (long long)kv * xs + 8 * sub);
+      if constexpr (PAGED) {  // row r0 + u RSTEP of the tile's page
+        const uint16_t* Xt = X + (v_rows ? s_voff[t] : s_koff[t]);
+        if (kv < p.Skv) v = *(const u32x4_t*)(Xt + (long long)(r0 + u * RSTEP) * xs + 8 * sub);
+      } else {
+        if (kv < p.Skv) v = *(const u32x4_t*)(X + (long long)kv * xs + 8 * sub);
+      }
       x[u] = v;
     }
   };
@@ -189,18 +204,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     }
   };
   u32x4_t xa[U], xb[U];
-  load_rows(Kp, p.ks[2], 0, xa);
+  load_rows(Kp, p.ks[2], false, 0, xa);
   for (int base = 0; base < n_rows; base += 2 * STEP) {
     const bool second = base + STEP < n_rows;
-    if (second) load_rows(Kp, p.ks[2], base + STEP, xb);
+    if (second) load_rows(Kp, p.ks[2], false, base + STEP, xb);
     score_rows(base, xa);
     if (second) {
-      if (base + 2 * STEP < n_rows) load_rows(Kp, p.ks[2], base + 2 * STEP, xa);
+      if (base + 2 * STEP < n_rows) load_rows(Kp, p.ks[2], false, base + 2 * STEP, xa);
       score_rows(base + STEP, xb);
     }
   }
   __syncthreads();
-  load_rows(Vp, p.vs[2], 0, xa);  // first V rows, in flight during pass 2
+  load_rows(Vp, p.vs[2], true, 0, xa);  // first V rows, in flight during pass 2
 
   // ---- pass 2: per-head max, exponentials, sums --------------------------------
   float m[G], l[G];
@@ -265,10 +280,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   };
   for (int base = 0; base < n_rows; base += 2 * STEP) {
     const bool second = base + STEP < n_rows;
-    if (second) load_rows(Vp, p.vs[2], base + STEP, xb);
+    if (second) load_rows(Vp, p.vs[2], true, base + STEP, xb);
     pv_rows(base, xa);
     if (second) {
-      if (base + 2 * STEP < n_rows) load_rows(Vp, p.vs[2], base + 2 * STEP, xa);
+      if (base + 2 * STEP < n_rows) load_rows(Vp, p.vs[2], true, base + 2 * STEP, xa);
       pv_rows(base + STEP, xb);
     }
   }
@@ -359,7 +374,10 @@ struct LaunchDecode {
   template <class Score>
   void operator()() {
     dim3 grid(P.splits, P.f.Hkv, P.f.B);
-    hipLaunchKernelGGL((decode_partial_kernel<D, G, Score>), grid, dim3(kDecThreads), 0, stream, P);
+    if (P.page_table != nullptr)
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, Score, true>), grid, dim3(kDecThreads), 0, stream, P);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<D, G, Score, false>), grid, dim3(kDecThreads), 0, stream, P);
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(P.f.B * P.f.Hq), dim3(kDecThreads), 0, stream, P);
   }
 };

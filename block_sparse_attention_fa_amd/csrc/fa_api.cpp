@@ -81,6 +81,13 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
   if (a->Hq % a->Hkv != 0) return fail(FA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
   if (a->D != 64 && a->D != 128) return fail(FA_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", a->D);
   if (decode && a->Sq != 1) return fail(FA_ERR_SHAPE, "decode needs Sq == 1 (got %d)", a->Sq);
+  if (a->page_table != nullptr) {
+    if (!decode) return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is supported by fa_decode only");
+    if (a->num_pages <= 0) return fail(FA_ERR_SHAPE, "num_pages must be positive (got %d)", a->num_pages);
+    if (a->page_table_stride < ceil_div(a->Skv, FA_BLOCK))
+      return fail(FA_ERR_SHAPE, "page_table_stride %lld < ceil(Skv/128) = %d", (long long)a->page_table_stride,
+                  ceil_div(a->Skv, FA_BLOCK));
+  }
   fa_status st;
   if ((st = check_strides("q", a->q_stride, a->q)) != FA_OK) return st;
   if ((st = check_strides("k", a->k_stride, a->k)) != FA_OK) return st;
@@ -331,6 +338,9 @@ fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_byt
   P.blocks_per_split = plan.bps;
   P.ws_o = (float*)workspace;
   P.ws_lse = P.ws_o + (size_t)plan.splits * a->B * a->Hq * a->D;
+  P.page_table = a->page_table;
+  P.pt_stride = a->page_table_stride;
+  P.num_pages = a->num_pages;
   st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, (hipStream_t)stream);
   if (st != FA_OK) return fail(st, "decode launch failed");
   return FA_OK;

@@ -62,6 +62,9 @@ struct DecodeParams {
   int blocks_per_split; // kv tiles per split
   float* ws_o;          // [B, Hq, splits, D] fp32 (normalised partial outputs)
   float* ws_lse;        // [B, Hq, splits] fp32 base-2 LSE of each split
+  const int* page_table;  // nullptr: per-sequence caches; else page of (b, logical block)
+  long long pt_stride;    // page-table entries between sequences
+  int num_pages;
 };
 
 struct BuildParams {

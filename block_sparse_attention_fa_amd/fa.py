@@ -59,7 +59,8 @@ class AttnArgs(ctypes.Structure):
                 ("o_stride", c_int64 * 4),
                 ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("Sq", c_int32), ("Skv", c_int32),
                 ("D", c_int32), ("scale", c_float), ("block_mask", POINTER(BlockMaskC)),
-                ("score", ScoreDesc), ("num_splits", c_int32)]
+                ("score", ScoreDesc), ("num_splits", c_int32),
+                ("page_table", c_void_p), ("page_table_stride", c_int64), ("num_pages", c_int32)]
 
 
 # symbol -> (restype, argtypes)
@@ -238,14 +239,19 @@ def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, devi
     return bm
 
 
-def _check_tensors(q, k, v, out, lse):
+def _check_tensors(q, k, v, out, lse, paged=False):
     """What the C ABI cannot see from pointers and strides: dtypes, devices, and
-    the dims it takes from q and k alone (k's B and D, v's shape, out, lse)."""
+    the dims it takes from q and k alone (k's B and D, v's shape, out, lse).
+    With a paged cache, k and v are page pools [num_pages, Hkv, FA_BLOCK, D]."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t.dtype != torch.bfloat16 or t.dim() != 4:
             raise FAError(FA_ERR_SHAPE, f"{name} must be a 4-d torch.bfloat16 tensor")
-    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3] or tuple(v.shape) != tuple(k.shape):
+    if paged:
+        if k.shape[2] != FA_BLOCK or k.shape[3] != q.shape[3] or tuple(v.shape) != tuple(k.shape):
+            raise FAError(FA_ERR_SHAPE, f"page pools k {tuple(k.shape)} / v {tuple(v.shape)} must both be "
+                                        f"[num_pages, Hkv, {FA_BLOCK}, D={q.shape[3]}]")
+    elif k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3] or tuple(v.shape) != tuple(k.shape):
         raise FAError(FA_ERR_SHAPE, f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
     if tuple(out.shape) != tuple(q.shape):
         raise FAError(FA_ERR_SHAPE, f"out has shape {tuple(out.shape)}, q has {tuple(q.shape)}")
@@ -256,8 +262,9 @@ def _check_tensors(q, k, v, out, lse):
         raise FAError(FA_ERR_SHAPE, "every tensor must be on the GPU")
 
 
-def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits):
-    _check_tensors(q, k, v, out, lse)
+def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits, page_table=None):
+    import torch
+    _check_tensors(q, k, v, out, lse, paged=page_table is not None)
     a = AttnArgs()
     a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
     a.lse = lse.data_ptr() if lse is not None else None
@@ -267,6 +274,16 @@ def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits):
             arr[i] = s
     a.B, a.Hq, a.Sq, a.D = q.shape
     a.Hkv, a.Skv = k.shape[1], k.shape[2]
+    if page_table is not None:
+        if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_cuda \
+                or page_table.stride(1) != 1 or page_table.shape[0] < q.shape[0]:
+            raise FAError(FA_ERR_SHAPE, "page_table must be a torch.int32 [B, blocks] GPU tensor with unit "
+                                        "stride along blocks")
+        # logical capacity: the BlockMask's KV length, else every block of the table
+        a.Skv = block_mask.Skv if block_mask is not None else page_table.shape[1] * FA_BLOCK
+        a.page_table = page_table.data_ptr()
+        a.page_table_stride = page_table.stride(0)
+        a.num_pages = k.shape[0]
     a.scale = float(scale)
     a.block_mask = ctypes.pointer(block_mask.c) if block_mask is not None else None
     a.score = (score or ScoreMod()).desc()
@@ -285,20 +302,22 @@ def fa_forward(q, k, v, block_mask: BlockMask | None = None, score: ScoreMod | N
     return out
 
 
-def fa_decode_workspace_size(q, k, v, block_mask=None, score=None, num_splits=0):
-    a = _attn_args(q, k, v, q, None, block_mask, score, 0.0, num_splits)
+def fa_decode_workspace_size(q, k, v, block_mask=None, score=None, num_splits=0, page_table=None):
+    a = _attn_args(q, k, v, q, None, block_mask, score, 0.0, num_splits, page_table)
     n = c_size_t()
     _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return n.value
 
 
 def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
-              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None):
-    """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D]."""
+              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None, page_table=None):
+    """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D], or, with an int32
+    page_table [B, blocks], against page pools [num_pages, Hkv, 128, D] where
+    logical block j of sequence b is page page_table[b, j]."""
     import torch
     if out is None:
         out = torch.empty_like(q)
-    a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits)
+    a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits, page_table)
     n = c_size_t()
     _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 #define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
 
 typedef enum {
@@ -142,6 +142,20 @@ typedef struct {
   const fa_block_mask* block_mask; /* NULL => dense attention without a mask */
   fa_score_desc score;
   int32_t num_splits;         /* decode: max KV splits per sequence, 0 = auto; ignored by fa_forward */
+  /* Paged KV cache, fa_decode only (paper review §4.5 "PagedAttention support"
+   * and §5.4; talk summary, "Page Attention"): a compact pool of fixed-size pages
+   * reached through a page table.  NULL => k and v hold each sequence's cache
+   * [B,Hkv,Skv,D] as above.  Otherwise k and v point at page pools
+   * [num_pages, Hkv, FA_BLOCK, D] whose k_stride / v_stride are the (page, head,
+   * row, d) strides, and logical 128-key block j of sequence b is stored in page
+   * page_table[b * page_table_stride + j].  Skv is then the logical capacity
+   * (the BlockMask's KV length); the BlockMask, mask_mods and score_mods all see
+   * logical positions, and only blocks the BlockMask lists are looked up.
+   * Sequences may share pages.  Page ids outside [0, num_pages) are clamped into
+   * range (no fault, wrong values): the caller owns the table's validity. */
+  const int32_t* page_table;  /* device int32, >= B rows of page_table_stride entries */
+  int64_t page_table_stride;  /* entries between sequences, >= ceil(Skv / FA_BLOCK) */
+  int32_t num_pages;          /* pages in each pool */
 } fa_attn_args;
 
 /* Version of this ABI (FA_ABI_VERSION). */
@@ -178,7 +192,7 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE (sizes, Hq % Hkv, strides, BlockMask dims,
  * Bm/Hm not in {1,B}/{1,Hq}, a batch-dependent mask with Bm = 1 < B, a BlockMask
  * built for other lengths), FA_ERR_UNSUPPORTED (D, alignment, kinds, bias
- * stride[3] != 1), FA_ERR_HIP. */
+ * stride[3] != 1, a page table), FA_ERR_HIP. */
 fa_status fa_forward(const fa_attn_args* a, void* stream);
 
 /* Host only.  Bytes of decode workspace fa_decode needs for these arguments
@@ -196,7 +210,10 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
  * size Hq/Hkv must be 1, 2, 4 or 8, and 1 when Hm > 1.  num_splits (0 = auto)
  * sets how many chunks a sequence is cut into; a chunk holds 1 to 8 tiles, so
  * the split count used is ceil(NK / clamp(ceil(NK / num_splits), 1, 8)).
- * Errors: as fa_forward, plus FA_ERR_SHAPE for Sq != 1 and FA_ERR_WORKSPACE. */
+ * With a page table (see fa_attn_args) the K/V rows of each listed block are
+ * read from its page; the arithmetic is otherwise unchanged.
+ * Errors: as fa_forward, plus FA_ERR_SHAPE for Sq != 1, num_pages <= 0 or
+ * page_table_stride < ceil(Skv / FA_BLOCK), and FA_ERR_WORKSPACE. */
 fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 1
+    assert L.fa_abi_version() == 2
     for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                                  "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
         assert L.fa_status_string(code).decode() == name
@@ -176,3 +176,20 @@ def test_binding_rejects_mismatched_tensors():
         with pytest.raises(fa.FAError) as e:
             fa.fa_forward(c["q"], c["k"], c["v"], out=c.get("out"), lse=c.get("lse"))
         assert e.value.status == fa.FA_ERR_SHAPE, c
+
+
+def test_paged_cache_validation():
+    """A page table is for fa_decode only; its page count and row stride are checked on the host."""
+    a = _args(Hq=4, Hkv=1, Sq=1, Skv=1000, D=128)
+    a.page_table = 0x20000
+    a.num_pages = 16
+    a.page_table_stride = 8                       # ceil(1000 / 128) = 8
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED    # fa_forward
+    n = ctypes.c_size_t()
+    assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    assert n.value > 0
+    a.page_table_stride = 7
+    assert _status(a, decode=True) == fa.FA_ERR_SHAPE
+    a.page_table_stride = 8
+    a.num_pages = 0
+    assert _status(a, decode=True) == fa.FA_ERR_SHAPE

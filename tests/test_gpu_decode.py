@@ -105,3 +105,71 @@ def test_empty_sequence_strided_cache_and_scale():
     C.compare(got, O, "decode strided")
     C.compare_lse(gl[..., 0], L[..., 0], "decode strided")
     assert np.all(got[1] == 0.0) and np.all(np.isneginf(gl[1]))
+
+
+def _page_pools(k, v, lens, seed, share_first_page=False):
+    """Scatter per-sequence caches [B,Hkv,KV,D] (bf16 bits) into shuffled page pools
+    [P,Hkv,128,D] with a page table, the way a serving cache holds them: only the
+    pages a sequence needs, in no particular order, with spare pages holding other
+    data.  Returns the pools, the table and the logical caches the table
+    describes (the oracle's input)."""
+    B, Hkv, KV, D = k.shape
+    nkb = -(-KV // 128)
+    need = [-(-int(n) // 128) for n in lens]
+    P = sum(need) + 3
+    rng = np.random.default_rng([seed, 5])
+    perm = rng.permutation(P)
+    k_pool = gen._normal_bf16([seed, 6], (P, Hkv, 128, D), 1.0)   # spare pages: other finite data
+    v_pool = gen._normal_bf16([seed, 7], (P, Hkv, 128, D), 1.0)
+    table = np.full((B, nkb + 2), P + 1000, dtype=np.int32)       # entries past a sequence are never read
+    i = 0
+    for b in range(B):
+        for j in range(need[b]):
+            pg, rows = perm[i], min(128, KV - 128 * j)
+            k_pool[pg, :, :rows] = k[b, :, 128 * j:128 * j + rows]
+            v_pool[pg, :, :rows] = v[b, :, 128 * j:128 * j + rows]
+            table[b, j] = pg
+            i += 1
+    if share_first_page:  # sequences 1.. reuse sequence 0's first page (a shared prompt prefix)
+        table[1:, 0] = table[0, 0]
+    k_log = np.zeros_like(k)
+    v_log = np.zeros_like(v)
+    for b in range(B):
+        for j in range(need[b]):
+            rows = min(128, KV - 128 * j)
+            k_log[b, :, 128 * j:128 * j + rows] = k_pool[table[b, j], :, :rows]
+            v_log[b, :, 128 * j:128 * j + rows] = v_pool[table[b, j], :, :rows]
+    return k_pool, v_pool, table, k_log, v_log
+
+
+@pytest.mark.parametrize("G,D,score", [(4, 128, "softcap"), (1, 64, "alibi"), (8, 128, "none")])
+@pytest.mark.parametrize("share", [False, True])
+def test_paged_decode(G, D, score, share):
+    """Paged decode equals the oracle on the logical caches the page table
+    describes, and equals contiguous decode on those caches bit for bit (same
+    chunks, same arithmetic, only the row addresses differ)."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    print(f"[case] paged decode G={G} D={D} score={score} shared={share}", flush=True)
+    B, Hkv, KV = 3, 2, 1500
+    Hq = G * Hkv
+    q = gen.qkv(80 + G, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(81 + G, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([1500, 700, 129], dtype=np.int32)
+    k_pool, v_pool, table, k_log, v_log = _page_pools(k, v, lens, 90 + G, share)
+    spec = C.make_spec(82, "kv_len", score, B, Hq, 1, KV, cap=50.0)
+    spec["lens"] = lens
+    sc = C.gpu_score(spec)
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    qt = gen.to_torch_bf16(q)
+    out = fa.fa_decode(qt, gen.to_torch_bf16(k_pool), gen.to_torch_bf16(v_pool), block_mask=bm, score=sc,
+                       lse=lse, page_table=torch.from_numpy(table).cuda())
+    lse_c = torch.empty_like(lse)
+    out_c = fa.fa_decode(qt, gen.to_torch_bf16(k_log), gen.to_torch_bf16(v_log), block_mask=bm, score=sc, lse=lse_c)
+    torch.cuda.synchronize()
+    got = gen.bf16_bits_to_f32(gen.from_torch_bf16(out))
+    O, L = fo.decode(q, k_log, v_log, lens, C.oracle_score(spec, Hq))
+    C.compare(got, O, "paged decode")
+    C.compare_lse(lse.cpu().numpy()[..., 0], L[..., 0], "paged decode")
+    assert torch.equal(out, out_c) and torch.equal(lse, lse_c)
