@@ -58,6 +58,13 @@ def bf16_to_f64(bits) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def _values(x) -> np.ndarray:
+    """Tensor values as float64: bfloat16 bit patterns are decoded, float64
+    arrays (used by the finite-difference pins) are taken as they are."""
+    x = np.asarray(x)
+    return x if x.dtype == np.float64 else bf16_to_f64(x)
+
+
 # ---------------------------------------------------------------------------
 # mask_mods: mask(b, h, q_idx, kv_idx) -> bool, True = attend.
 # Signature from Concepts "mask_mod" and paper review §2.2; indices are
@@ -142,20 +149,33 @@ def default_alibi_slopes(H: int) -> np.ndarray:
     return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float64)
 
 
+def _with_grad(mod, grad):
+    """Attach d mod / d s (used by the backward; the forward never calls it)."""
+    mod.grad = grad
+    return mod
+
+
+def _unit_grad(s, b, h, q, kv):
+    """Derivative of an additive score_mod (s + something that does not depend on s)."""
+    return np.ones_like(np.asarray(s, dtype=np.float64))
+
+
 def alibi(slopes):
     """Concepts "score_mod": score + slope[h] * (kv - q)."""
     sl = np.asarray(slopes, dtype=np.float64)
-    return lambda s, b, h, q, kv: s + sl[h] * (kv - q)
+    return _with_grad(lambda s, b, h, q, kv: s + sl[h] * (kv - q), _unit_grad)
 
 
 def softcap(cap: float):
-    """Paper review §2.1 table (Softcapping), Concepts notebook list: cap * tanh(s / cap)."""
-    return lambda s, b, h, q, kv: cap * np.tanh(s / cap)
+    """Paper review §2.1 table (Softcapping), Concepts notebook list: cap * tanh(s / cap).
+    Its derivative is 1 - tanh(s / cap)^2."""
+    return _with_grad(lambda s, b, h, q, kv: cap * np.tanh(s / cap),
+                      lambda s, b, h, q, kv: 1.0 - np.tanh(s / cap) ** 2)
 
 
 def rel_pos():
     """Talk summary (score mode) / Concepts "Debugging score_mods": score + (q - kv)."""
-    return lambda s, b, h, q, kv: s + (q - kv)
+    return _with_grad(lambda s, b, h, q, kv: s + (q - kv), _unit_grad)
 
 
 def bias(table):
@@ -165,7 +185,7 @@ def bias(table):
     bfloat16 bit patterns (a uint16 array, possibly with size-1 broadcast
     dims, or any object with that __getitem__).
     """
-    return lambda s, b, h, q, kv: s + bf16_to_f64(table[b, h, q, kv])
+    return _with_grad(lambda s, b, h, q, kv: s + bf16_to_f64(table[b, h, q, kv]), _unit_grad)
 
 
 # ---------------------------------------------------------------------------
@@ -192,9 +212,9 @@ def attention_rows(q, k, v, b: int, hq: int, rows, mask_mod=None, score_mod=None
         scale = 1.0 / math.sqrt(D)
     rows = np.asarray(rows, dtype=np.int64)
 
-    Q = bf16_to_f64(q[b, hq, rows])                 # [R, D]
-    K = bf16_to_f64(k[b, hkv])                      # [Skv, D]
-    V = bf16_to_f64(v[b, hkv])                      # [Skv, D]
+    Q = _values(q[b, hq, rows])                     # [R, D]
+    K = _values(k[b, hkv])                          # [Skv, D]
+    V = _values(v[b, hkv])                          # [Skv, D]
 
     S = (Q @ K.T) * scale                           # step 1
     qi = rows[:, None]
@@ -254,6 +274,71 @@ def decode(q, k_cache, v_cache, lengths, score_mod=None, scale=None, extra_mask=
 
 
 # ---------------------------------------------------------------------------
+# Attention backward (gradients of the definition above, dense, fp64)
+# ---------------------------------------------------------------------------
+
+def attention_backward(q, k, v, dout, mask_mod=None, score_mod=None, scale=None):
+    """dQ, dK, dV of the forward definition for an upstream gradient dO.
+
+    The pages name a backward pass and its transposed BlockMask view (Concepts
+    "Key attributes": q_num_blocks / q_indices, "used in backward") but print
+    no formulas, so this is the chain rule taken through the forward's steps
+    one by one, for each (b, hq) with its KV head hkv:
+      forward:  S = Q K^T * scale;  S' = mod(S) where kept, -inf elsewhere;
+                P = softmax_kv(S');  O = P V
+      backward: dV[hkv] += P^T dO
+                dP = dO V^T
+                dS' = P * (dP - rowsum(P * dP))        (softmax Jacobian)
+                dS = dS' * mod'(S) where kept, 0 elsewhere
+                dQ = scale * dS K;  dK[hkv] += scale * dS^T Q
+    A row with every position masked has P = 0 and contributes nothing.
+    Inputs are bfloat16 bits or float64 arrays; returns float64 arrays shaped
+    like q, k, v.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dQ = np.zeros((B, Hq, Sq, D))
+    dK = np.zeros((B, Hkv, Skv, D))
+    dV = np.zeros((B, Hkv, Skv, D))
+    qi = np.arange(Sq, dtype=np.int64)[:, None]
+    ki = np.arange(Skv, dtype=np.int64)[None, :]
+    for b in range(B):
+        for hq in range(Hq):
+            hkv = hq // (Hq // Hkv)
+            Q, K, V = _values(q[b, hq]), _values(k[b, hkv]), _values(v[b, hkv])
+            dO = _values(dout[b, hq])
+            S = scale * (Q @ K.T)
+            if mask_mod is None:
+                M = np.ones(S.shape, dtype=bool)
+            else:
+                M = np.broadcast_to(np.asarray(mask_mod(b, hq, qi, ki), dtype=bool), S.shape)
+            qb, kb = np.broadcast_arrays(qi, ki)
+            Sp = np.full_like(S, NEG_INF)
+            grad_mod = np.zeros(S.shape)
+            if score_mod is None:
+                Sp[M] = S[M]
+                grad_mod[M] = 1.0
+            else:
+                kept = (S[M], b, hq, qb[M], kb[M])
+                Sp[M] = score_mod(*kept)
+                grad_mod[M] = score_mod.grad(*kept)
+            m = Sp.max(axis=1)
+            P = np.zeros(S.shape)
+            live = m > NEG_INF
+            E = np.exp(Sp[live] - m[live, None])
+            P[live] = E / E.sum(axis=1, keepdims=True)
+            dV[b, hkv] += P.T @ dO
+            dP = dO @ V.T
+            dSp = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dS = dSp * grad_mod
+            dQ[b, hq] = scale * (dS @ K)
+            dK[b, hkv] += scale * (dS.T @ Q)
+    return dQ, dK, dV
+
+
+# ---------------------------------------------------------------------------
 # BlockMask (Concepts "BlockMask Internals" / "Key attributes"; paper review §4.1-4.2)
 # ---------------------------------------------------------------------------
 
@@ -299,20 +384,27 @@ def _compact(sel: np.ndarray):
 
 def block_mask(mask_mod, Bm: int, Hm: int, Sq: int, Skv: int, block: int = 128,
                separate_full: bool = True):
-    """The four BlockMask tensors of Concepts "Key attributes".
+    """The BlockMask tensors of Concepts "Key attributes".
 
     separate_full=True (canonical): kv_* lists PARTIAL tiles only and full_*
     lists FULL tiles only.  separate_full=False: kv_* lists every non-empty
-    tile and full_* the FULL ones among them.
+    tile and full_* the FULL ones among them.  q_* and full_q_* are the same
+    lists seen per KV block (q blocks ascending, padded with 0, last dim NQ).
     """
     cls = block_classes(mask_mod, Bm, Hm, Sq, Skv, block)
     full = cls == FULL
     kv_sel = (cls == PARTIAL) if separate_full else (cls != EMPTY)
     kv_num, kv_idx = _compact(kv_sel)
     full_num, full_idx = _compact(full)
+    # Transposed view (Concepts "Key attributes": q_num_blocks / q_indices, for
+    # the backward): per KV block, the query blocks of the same lists, ascending.
+    q_num, q_idx = _compact(np.swapaxes(kv_sel, -1, -2))
+    full_q_num, full_q_idx = _compact(np.swapaxes(full, -1, -2))
     return {
         "kv_num_blocks": kv_num, "kv_indices": kv_idx,
         "full_kv_num_blocks": full_num, "full_kv_indices": full_idx,
+        "q_num_blocks": q_num, "q_indices": q_idx,
+        "full_q_num_blocks": full_q_num, "full_q_indices": full_q_idx,
         "classes": cls,
     }
 

@@ -46,6 +46,20 @@ MUTANTS = [
      "return prefix(prefix_len)", [pins.test_mask_limits]),
     ("doc_ignores_batch", "doc[b, q] == doc[b, kv]", "doc[0, q] == doc[0, kv]",
      [lambda: pins.test_oracle_matches_sdpa_boolean_masks(16, "document")]),
+    ("bwd_drop_softmax_jacobian_term", "dSp = P * (dP - (P * dP).sum(axis=1, keepdims=True))", "dSp = P * dP",
+     [lambda: pins.test_backward_matches_torch_autograd_sdpa("causal")]),
+    ("bwd_ignore_mod_derivative", "dS = dSp * grad_mod", "dS = dSp * (grad_mod != 0)",
+     [pins.test_backward_softcap_matches_torch_autograd]),
+    ("bwd_dq_unscaled", "dQ[b, hq] = scale * (dS @ K)", "dQ[b, hq] = dS @ K",
+     [lambda: pins.test_backward_matches_torch_autograd_sdpa("none")]),
+    ("bwd_dk_untransposed", "dK[b, hkv] += scale * (dS.T @ Q)", "dK[b, hkv] += scale * (dS @ Q)",
+     [lambda: pins.test_backward_matches_torch_autograd_sdpa("alibi_causal")]),
+    ("bwd_dv_overwrites_group", "dV[b, hkv] += P.T @ dO", "dV[b, hkv] = P.T @ dO",
+     [pins.test_backward_gqa_equals_mha_summed_over_the_group]),
+    ("bwd_unnormalised_p", "P[live] = E / E.sum(axis=1, keepdims=True)", "P[live] = E",
+     [lambda: pins.test_backward_matches_finite_differences("causal", "none")]),
+    ("transposed_lists_of_full_tiles", "q_num, q_idx = _compact(np.swapaxes(kv_sel, -1, -2))",
+     "q_num, q_idx = _compact(np.swapaxes(full, -1, -2))", [pins.test_transposed_block_lists]),
 ]
 
 

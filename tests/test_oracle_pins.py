@@ -485,3 +485,151 @@ def test_blockmask_memory_ratio():
     S = 8192
     cls = fo.block_classes(fo.causal(), 1, 1, S, S)
     assert (S * S) / cls.size == 16384
+
+
+# ---------------------------------------------------------------------------
+# Backward (attention_backward): finite differences, torch autograd, closed forms
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, dO, om, sm, scale):
+    O, _ = fo.attention(q, k, v, om, sm, scale=scale)
+    return float((O * dO).sum())
+
+
+@pytest.mark.parametrize("mname", ["causal", "sliding_causal2", "document_causal", "kv_len", "none"])
+@pytest.mark.parametrize("sname", list(MODS))
+def test_backward_matches_finite_differences(mname, sname):
+    """Central differences of L = sum(O * dO) with respect to sampled entries of
+    Q, K and V (float64 inputs, tiny GQA shapes), against the analytic gradients."""
+    q, k, v = (fo.bf16_to_f64(x) for x in _tiny(7))
+    om, sm = MASKS[mname][0], MODS[sname][0]
+    scale = 1.0 / math.sqrt(8)
+    rng = np.random.default_rng([21, len(mname), len(sname)])
+    dO = rng.standard_normal(q.shape)
+    grads = fo.attention_backward(q, k, v, dO, om, sm, scale)
+    eps = 1e-6
+    for x, g in zip((q, k, v), grads):
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            up = _loss(q, k, v, dO, om, sm, scale)
+            x[idx] = x0 - eps
+            dn = _loss(q, k, v, dO, om, sm, scale)
+            x[idx] = x0
+            np.testing.assert_allclose(g[idx], (up - dn) / (2 * eps), rtol=1e-5, atol=1e-8,
+                                       err_msg=f"{mname}/{sname} at {idx}")
+
+
+def _torch_grads(q, k, v, dO, fn):
+    qt, kt, vt = (torch.from_numpy(fo.bf16_to_f64(x)).requires_grad_() for x in (q, k, v))
+    out = fn(qt, kt, vt)
+    out.backward(torch.from_numpy(dO))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("case", ["causal", "document", "alibi_causal", "bias_causal", "none"])
+def test_backward_matches_torch_autograd_sdpa(case):
+    """torch autograd through its CPU scaled_dot_product_attention (float64, GQA)."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 70, 16
+    q, k, v = gen.qkv(31, B, Hq, Hkv, S, S, D)
+    dO = np.random.default_rng(31).standard_normal((B, Hq, S, D))
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    docs = gen.document_ids(31, B, S, 10, 30)
+    slopes = fo.default_alibi_slopes(Hq)
+    bias_bits = gen._normal_bf16([31, 16], (B, Hq, S, S), 0.5)
+    if case == "causal":
+        om, sm, tm = fo.causal(), None, torch.from_numpy(i >= j)
+    elif case == "document":
+        om, sm = fo.document(docs), None
+        tm = torch.from_numpy(docs[:, :, None] == docs[:, None, :])[:, None]
+    elif case == "alibi_causal":
+        om, sm = fo.causal(), fo.alibi(slopes)
+        tm = torch.from_numpy(np.where((i >= j)[None], slopes[:, None, None] * (j - i), -np.inf))
+    elif case == "bias_causal":
+        om, sm = fo.causal(), fo.bias(bias_bits)
+        tm = torch.from_numpy(np.where((i >= j)[None, None], fo.bf16_to_f64(bias_bits), -np.inf))
+    else:
+        om, sm, tm = None, None, None
+    ref = _torch_grads(q, k, v, dO, lambda a, b_, c: torch.nn.functional.scaled_dot_product_attention(
+        a, b_, c, attn_mask=tm, enable_gqa=True))
+    got = fo.attention_backward(q, k, v, dO, om, sm)
+    for name, g, r in zip("QKV", got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-11, err_msg=f"d{name} {case}")
+
+
+def test_backward_softcap_matches_torch_autograd():
+    """Softcap is no SDPA mask, so the reference is torch autograd through the
+    forward written with torch ops (scale, cap*tanh(s/cap), causal -inf, softmax)."""
+    B, Hq, Hkv, S, D, cap = 1, 2, 1, 50, 16, 0.8
+    q, k, v = gen.qkv(33, B, Hq, Hkv, S, S, D)
+    dO = np.random.default_rng(33).standard_normal((B, Hq, S, D))
+    keep = torch.from_numpy(np.arange(S)[:, None] >= np.arange(S)[None, :])
+
+    def fwd(a, b_, c):
+        b_, c = b_.repeat_interleave(Hq // Hkv, dim=1), c.repeat_interleave(Hq // Hkv, dim=1)
+        s = (a @ b_.transpose(-1, -2)) / math.sqrt(D)
+        s = cap * torch.tanh(s / cap)
+        return torch.softmax(s.masked_fill(~keep, -math.inf), dim=-1) @ c
+
+    ref = _torch_grads(q, k, v, dO, fwd)
+    got = fo.attention_backward(q, k, v, dO, fo.causal(), fo.softcap(cap))
+    for name, g, r in zip("QKV", got, ref):
+        np.testing.assert_allclose(g, r, rtol=0, atol=1e-11, err_msg=f"d{name} softcap")
+
+
+def test_backward_closed_forms():
+    """Uniform V: O does not depend on Q or K, so dQ = dK = 0 and dV sums
+    P^T dO.  Causal row 0 attends one key: its dO flows to dV[0] unchanged."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 33, 8
+    q, k, v = gen.qkv(35, B, Hq, Hkv, S, S, D)
+    v[:] = v[:, :, :1, :]                                  # every V row equal
+    dO = np.random.default_rng(35).standard_normal((B, Hq, S, D))
+    dQ, dK, dV = fo.attention_backward(q, k, v, dO, fo.causal(), fo.alibi(fo.default_alibi_slopes(Hq)))
+    np.testing.assert_allclose(dQ, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dK, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dV.sum(axis=2), dO.sum(axis=(1, 2))[:, None, :], rtol=0, atol=1e-11)
+    dO0 = np.zeros_like(dO)
+    dO0[:, :, 0] = dO[:, :, 0]
+    _, _, dV0 = fo.attention_backward(q, k, v, dO0, fo.causal())
+    np.testing.assert_allclose(dV0[:, 0, 0], dO[:, :, 0].sum(axis=1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dV0[:, 0, 1:], 0.0, atol=1e-12)
+
+
+def test_backward_gqa_equals_mha_summed_over_the_group():
+    B, Hq, Hkv, S, D = 1, 4, 2, 40, 8
+    q, k, v = gen.qkv(37, B, Hq, Hkv, S, S, D)
+    dO = np.random.default_rng(37).standard_normal((B, Hq, S, D))
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    sm = fo.softcap(2.0)
+    dQ1, dK1, dV1 = fo.attention_backward(q, k, v, dO, fo.causal(), sm)
+    dQ2, dK2, dV2 = fo.attention_backward(q, kr, vr, dO, fo.causal(), sm)
+    np.testing.assert_allclose(dQ1, dQ2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dK1, dK2.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dV1, dV2.reshape(B, Hkv, Hq // Hkv, S, D).sum(axis=2), rtol=0, atol=1e-13)
+
+
+def test_backward_fully_masked_row_contributes_nothing():
+    q, k, v = _tiny(3)
+    dO = np.random.default_rng(3).standard_normal(q.shape)
+    dQ, dK, dV = fo.attention_backward(q, k, v, dO, fo.kv_length(np.array([4, 0])))
+    assert np.all(dQ[1] == 0.0) and np.all(dK[1] == 0.0) and np.all(dV[1] == 0.0)
+    assert np.all(np.isfinite(dQ)) and np.abs(dQ[0]).max() > 0
+
+
+def test_transposed_block_lists():
+    """q_* / full_q_* list, per KV block, the query blocks whose row lists hold it."""
+    docs = gen.document_ids(43, 1, 300, 20, 90)
+    for om in (fo.causal(), fo.sliding_causal(100), fo.document_causal(docs)):
+        for sep in (True, False):
+            bm = fo.block_mask(om, 1, 1, 300, 260, block=32, separate_full=sep)
+            NQ, NK = bm["kv_num_blocks"].shape[-1], bm["q_num_blocks"].shape[-1]
+            for kb in range(NK):
+                rows = [qb for qb in range(NQ) if kb in bm["kv_indices"][0, 0, qb, :bm["kv_num_blocks"][0, 0, qb]]]
+                full = [qb for qb in range(NQ)
+                        if kb in bm["full_kv_indices"][0, 0, qb, :bm["full_kv_num_blocks"][0, 0, qb]]]
+                assert bm["q_num_blocks"][0, 0, kb] == len(rows)
+                assert list(bm["q_indices"][0, 0, kb]) == rows + [0] * (NQ - len(rows))
+                assert bm["full_q_num_blocks"][0, 0, kb] == len(full)
+                assert list(bm["full_q_indices"][0, 0, kb]) == full + [0] * (NQ - len(full))
