@@ -115,6 +115,54 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(BuildParams 
   }
 }
 
+// Transposed view (Concepts "Key attributes": q_num_blocks / q_indices, "used
+// in backward"): for KV block kb, the query blocks whose row lists hold kb, in
+// ascending order, padded with 0.  One wave per (b', h', kb); its lanes take 64
+// query blocks at a time and binary-search kb in their (ascending) row lists,
+// so the columns agree with the rows by construction.
+__device__ __forceinline__ bool list_has(const int* idx, int n, int kb) {
+  int lo = 0, hi = n;  // first entry >= kb in [lo, hi)
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (idx[mid] < kb) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && idx[lo] == kb;
+}
+
+__global__ __launch_bounds__(64) void transpose_block_lists_kernel(BuildParams p) {
+  const int kb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const long long bh = (long long)b * p.Hm + h;
+  const long long col = bh * p.NK + kb;
+  int* q_idx = p.q_idx + col * p.NQ;
+  int* full_q_idx = p.full_q_idx + col * p.NQ;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int np = 0, nf = 0;
+  for (int q0 = 0; q0 < p.NQ; q0 += 64) {
+    const int qb = q0 + lane;
+    bool in_kv = false, in_full = false;
+    if (qb < p.NQ) {
+      const long long row = bh * p.NQ + qb;
+      in_kv = list_has(p.kv_idx + row * p.NK, p.kv_num[row], kb);
+      in_full = list_has(p.full_idx + row * p.NK, p.full_num[row], kb);
+    }
+    const unsigned long long mk = __ballot(in_kv);
+    const unsigned long long mf = __ballot(in_full);
+    if (in_kv) q_idx[np + __popcll(mk & below)] = qb;
+    if (in_full) full_q_idx[nf + __popcll(mf & below)] = qb;
+    np += __popcll(mk);
+    nf += __popcll(mf);
+  }
+  for (int i = lane; i < p.NQ; i += 64) {
+    if (i >= np) q_idx[i] = 0;
+    if (i >= nf) full_q_idx[i] = 0;
+  }
+  if (lane == 0) {
+    p.q_num[col] = np;
+    p.full_q_num[col] = nf;
+  }
+}
+
 struct LaunchBuild {
   const BuildParams& p;
   hipStream_t stream;
@@ -122,6 +170,8 @@ struct LaunchBuild {
   void operator()() {
     dim3 grid(p.NQ, p.Hm, p.Bm);
     hipLaunchKernelGGL(build_block_mask_kernel<Mask>, grid, dim3(kThreads), 0, stream, p);
+    if (p.q_num != nullptr)
+      hipLaunchKernelGGL(transpose_block_lists_kernel, dim3(p.NK, p.Hm, p.Bm), dim3(64), 0, stream, p);
   }
 };
 

@@ -279,6 +279,11 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   if (bm->Bm < 1 || bm->Hm < 1 || bm->Bm > 65535 || bm->Hm > 65535)
     return fail(FA_ERR_SHAPE, "Bm and Hm must be in [1, 65535]");
   if (bm->separate_full != 0 && bm->separate_full != 1) return fail(FA_ERR_SHAPE, "separate_full must be 0 or 1");
+  const int n_transposed = (bm->q_num_blocks != nullptr) + (bm->q_indices != nullptr) +
+                           (bm->full_q_num_blocks != nullptr) + (bm->full_q_indices != nullptr);
+  if (n_transposed != 0 && n_transposed != 4)
+    return fail(FA_ERR_NULL, "the transposed view needs all four of q_num_blocks, q_indices, "
+                             "full_q_num_blocks and full_q_indices (or none)");
   fa_status st = check_mask(bm->mask, Sq, Skv);
   if (st != FA_OK) return st;
 
@@ -287,6 +292,10 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   p.kv_idx = bm->kv_indices;
   p.full_num = bm->full_kv_num_blocks;
   p.full_idx = bm->full_kv_indices;
+  p.q_num = bm->q_num_blocks;
+  p.q_idx = bm->q_indices;
+  p.full_q_num = bm->full_q_num_blocks;
+  p.full_q_idx = bm->full_q_indices;
   p.Bm = bm->Bm;
   p.Hm = bm->Hm;
   p.NQ = bm->NQ;

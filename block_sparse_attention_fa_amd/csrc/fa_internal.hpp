@@ -72,6 +72,10 @@ struct BuildParams {
   int* kv_idx;
   int* full_num;
   int* full_idx;
+  int* q_num;       // transposed view, all four nullptr when not requested
+  int* q_idx;
+  int* full_q_num;
+  int* full_q_idx;
   int Bm, Hm, NQ, NK, Sq, Skv;
   int separate_full;
   MaskParams mask;

@@ -50,7 +50,9 @@ class BlockMaskC(ctypes.Structure):
                 ("full_kv_num_blocks", c_void_p), ("full_kv_indices", c_void_p),
                 ("Bm", c_int32), ("Hm", c_int32), ("NQ", c_int32), ("NK", c_int32),
                 ("block_q", c_int32), ("block_kv", c_int32), ("separate_full", c_int32),
-                ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc)]
+                ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc),
+                ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
+                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -161,7 +163,7 @@ class ScoreMod:
 class BlockMask:
     """Device BlockMask: the four int32 tensors of the Concepts page's "Key attributes"."""
 
-    def __init__(self, mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda"):
+    def __init__(self, mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", transposed=False):
         import torch
         NQ, NK = fa_block_mask_dims(Sq, Skv)
         self.mask = mask
@@ -180,6 +182,15 @@ class BlockMask:
         c.block_q = c.block_kv = FA_BLOCK
         c.separate_full = 1 if separate_full else 0
         c.mask = mask.desc()
+        # transposed view (q_num_blocks / q_indices, for the backward), built on request
+        self.transposed = bool(transposed)
+        if self.transposed:
+            self.q_num_blocks = torch.empty((Bm, Hm, NK), **z)
+            self.q_indices = torch.empty((Bm, Hm, NK, NQ), **z)
+            self.full_q_num_blocks = torch.empty((Bm, Hm, NK), **z)
+            self.full_q_indices = torch.empty((Bm, Hm, NK, NQ), **z)
+            c.q_num_blocks, c.q_indices = self.q_num_blocks.data_ptr(), self.q_indices.data_ptr()
+            c.full_q_num_blocks, c.full_q_indices = self.full_q_num_blocks.data_ptr(), self.full_q_indices.data_ptr()
 
     def list_every_tile(self):
         """Re-encode as "no block skipping": every tile of every row is listed as
@@ -192,11 +203,19 @@ class BlockMask:
                               .expand_as(self.kv_indices))
         self.separate_full = False
         self.c.separate_full = 0
+        if self.transposed:
+            self.q_num_blocks.fill_(self.NQ)
+            self.q_indices.copy_(torch.arange(self.NQ, dtype=torch.int32, device=self.q_indices.device)
+                                 .expand_as(self.q_indices))
         return self
 
     def tensors(self):
-        return {"kv_num_blocks": self.kv_num_blocks, "kv_indices": self.kv_indices,
-                "full_kv_num_blocks": self.full_kv_num_blocks, "full_kv_indices": self.full_kv_indices}
+        t = {"kv_num_blocks": self.kv_num_blocks, "kv_indices": self.kv_indices,
+             "full_kv_num_blocks": self.full_kv_num_blocks, "full_kv_indices": self.full_kv_indices}
+        if self.transposed:
+            t.update({"q_num_blocks": self.q_num_blocks, "q_indices": self.q_indices,
+                      "full_q_num_blocks": self.full_q_num_blocks, "full_q_indices": self.full_q_indices})
+        return t
 
     def classes(self):
         """int8 [Bm,Hm,NQ,NK] on the host: 0 empty, 1 partial, 2 full (decoded from the lists)."""
@@ -232,9 +251,11 @@ def fa_block_mask_dims(Sq, Skv, block_q=FA_BLOCK, block_kv=FA_BLOCK):
     return nq.value, nk.value
 
 
-def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", stream=None):
-    """Allocate a BlockMask and build it on the device (asynchronously on `stream`)."""
-    bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device)
+def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", stream=None,
+                        transposed=False):
+    """Allocate a BlockMask and build it on the device (asynchronously on `stream`);
+    transposed=True also builds the per-KV-block view the backward needs."""
+    bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed)
     _check(lib().fa_build_block_mask(ctypes.byref(bm.c), Sq, Skv, _stream(stream)))
     return bm
 

@@ -123,6 +123,17 @@ typedef struct {
   int32_t separate_full;     /* 1 = disjoint lists (canonical), 0 = superset */
   int32_t Sq, Skv;           /* set by fa_build_block_mask; fa_forward checks them */
   fa_mask_desc mask;
+  /* Transposed view (Concepts "Key attributes": q_num_blocks / q_indices, used by
+   * the backward): for each KV block, the query blocks of the lists above, in
+   * ascending order and padded with 0.  q_* is the view of kv_* (partial tiles,
+   * or every non-empty one when separate_full = 0) and full_q_* the view of
+   * full_kv_*.  Optional: either all four are NULL, or all four are device
+   * buffers that fa_build_block_mask fills.
+   * q_num_blocks, full_q_num_blocks: [Bm,Hm,NK]; q_indices, full_q_indices: [Bm,Hm,NK,NQ]. */
+  int32_t* q_num_blocks;
+  int32_t* q_indices;
+  int32_t* full_q_num_blocks;
+  int32_t* full_q_indices;
 } fa_block_mask;
 
 /* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]

@@ -193,3 +193,16 @@ def test_paged_cache_validation():
     a.page_table_stride = 8
     a.num_pages = 0
     assert _status(a, decode=True) == fa.FA_ERR_SHAPE
+
+
+def test_transposed_view_is_all_or_nothing():
+    """fa_build_block_mask fills the per-KV-block view only when all four buffers are given."""
+    c = fa.BlockMaskC()
+    c.kv_num_blocks = c.kv_indices = c.full_kv_num_blocks = c.full_kv_indices = 0x10000
+    c.Bm = c.Hm = 1
+    c.NQ = c.NK = 2
+    c.block_q = c.block_kv = fa.FA_BLOCK
+    c.separate_full = 1
+    c.mask = fa.MaskMod("causal").desc()
+    c.q_num_blocks = c.q_indices = 0x20000      # two of the four
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), 256, 256, None) == fa.FA_ERR_NULL

@@ -1,4 +1,5 @@
-"""BlockMask builder on the GPU vs the oracle: bit-exact over the whole tensors."""
+"""BlockMask builder on the GPU vs the oracle: bit-exact over the whole tensors,
+row lists and their transposed (per-KV-block) view."""
 
 import numpy as np
 import pytest
@@ -8,13 +9,15 @@ from oracle import flex_oracle as fo
 from tests import _cases as C
 
 pytestmark = pytest.mark.gpu
-KEYS = ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices")
+KEYS = ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices",
+        "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices")
 
 
 def _check_bitexact(spec, Bm, Hm, Sq, Skv, separate_full=True):
+    """Every list, the transposed (per-KV-block) view included, equals the oracle's."""
     from block_sparse_attention_fa_amd import fa
     import torch
-    bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full)
+    bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True)
     torch.cuda.synchronize()
     mm = C.oracle_mask(spec) or fo.no_mask()
     ref = fo.block_mask(mm, Bm, Hm, Sq, Skv, separate_full=separate_full)
