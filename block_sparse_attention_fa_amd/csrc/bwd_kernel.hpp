@@ -1,0 +1,546 @@
+// Block-sparse attention backward for CDNA4 (gfx950).
+//
+// The pages name a backward pass and the transposed BlockMask view it walks
+// (attention-gym "Concepts" page, "Key attributes": q_num_blocks / q_indices,
+// "used in backward"; paper review "Flex Attention: A Programming Model for
+// Generating Optimized Attention Kernels", kernel-template diagram) without
+// printing its formulas, so this is the gradient of the forward definition:
+// with S = Q K^T * scale, S' = mod(S) where the mask keeps (else -inf),
+// P = softmax(S') and O = P V,
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta) * mod'(S),
+//     dQ = scale * dS K,   dK = scale * dS^T Q,   Delta = rowsum(dO * O),
+// with P recomputed from the forward's log-sum-exp (no online softmax).
+//
+// Three kernels:
+//  * bwd_prep:  Delta and the base-2 LSE per query row, into a workspace padded
+//    to whole 128-row tiles (padded rows and rows that attend nothing get
+//    LSE = +inf, so their P is 0).
+//  * bwd_dq:    one workgroup per (b, hq, 128-row query tile), the forward's
+//    layout (4 waves x 32 query rows, a lane per query row): for every listed
+//    key tile, S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T with K^T
+//    read transposed from LDS (as the forward reads V^T).  Partial tiles
+//    evaluate the mask_mod, full tiles do not.
+//  * bwd_dkdv:  one workgroup per (b, hkv, 128-key tile), 4 waves x 32 keys, a
+//    lane per key; K and V stay in registers as MFMA B operands while the query
+//    tiles of the transposed lists (for every query head of the GQA group) stream
+//    through LDS: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T read transposed.  Its accumulators need
+//    more than 256 registers, so it runs one wave per SIMD.
+// No atomics: dQ and dK/dV come from separate passes (S and dP are computed
+// in both).
+#pragma once
+
+#include "fwd_kernel.hpp"
+
+namespace fa {
+
+constexpr int kBwdThreads = 256;
+
+// ---- bwd_prep: Delta = rowsum(dO * O) and LSE * log2(e) per query row --------------
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams P) {
+  const FwdParams& p = P.f;
+  const int lane = threadIdx.x & 63;
+  const long long gw = (long long)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);  // one wave per padded row
+  const int Sp = P.sq_pad;
+  if (gw >= (long long)p.B * p.Hq * Sp) return;
+  const int q = (int)(gw % Sp);
+  const int bh = (int)(gw / Sp);
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  float delta = 0.0f, lse2 = INFINITY;
+  if (q < p.Sq) {
+    const uint16_t* o = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)q * p.os[2];
+    const uint16_t* g = P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1] + (long long)q * P.dos[2];
+    float acc = 0.0f;
+    for (int d = lane; d < D; d += 64) acc = fmaf(bf16_bits_to_float(o[d]), bf16_bits_to_float(g[d]), acc);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    delta = acc;
+    const float l = p.lse[((long long)b * p.Hq + hq) * p.Sq + q];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+  if (lane == 0) {
+    P.ws_delta[gw] = delta;
+    P.ws_lse2[gw] = lse2;
+  }
+}
+
+// ---- bwd_dq ----------------------------------------------------------------------
+template <int D, class Mask, class Score>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams P) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int HB = 64;
+  constexpr int SPT = kBN / HB;
+  constexpr int NI = HB * CPR / 64 / 4;
+  const FwdParams& p = P.f;
+  // K and V sub-tiles, both row-major with the K chunk swizzle, 2-deep ring
+  __shared__ __align__(16) uint16_t k_lds[2][HB * D];
+  __shared__ __align__(16) uint16_t v_lds[2][HB * D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hh = lane >> 5;
+  const int gi = lane >> 4, si = lane & 15;
+
+  const int NQ = (p.Sq + kBM - 1) / kBM;
+  const int total = NQ * p.Hq * p.B;
+  const int L = xcd_logical_id(blockIdx.x, total);
+  const int qb = NQ - 1 - L % NQ;
+  const int bh = L / NQ;
+  const int hq = bh % p.Hq, b = bh / p.Hq;
+  const int hkv = hq / p.G;
+  const int q0 = qb * kBM;
+
+  const BlockMaskView& bm = p.bm;
+  int n_part, n_full;
+  const int* part_idx = nullptr;
+  const int* full_idx = nullptr;
+  if (bm.dense) {
+    n_part = 0;
+    n_full = bm.NK;
+  } else {
+    const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
+    const long long row = ((long long)mb * bm.Hm + mh) * bm.NQ + qb;
+    n_part = bm.kv_num[row];
+    part_idx = bm.kv_idx + row * bm.NK;
+    if (bm.separate_full) {
+      n_full = bm.full_num[row];
+      full_idx = bm.full_idx + row * bm.NK;
+    } else {
+      n_full = 0;
+    }
+  }
+  const int T = n_part + n_full;
+  auto kb_of = [&](int t) -> int {
+    if (t < n_part) return part_idx[t];
+    return bm.dense ? t - n_part : full_idx[t - n_part];
+  };
+
+  const char* Kp = (const char*)(p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1]);
+  const char* Vp = (const char*)(p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1]);
+  const long long ksb = 2 * p.ks[2], vsb = 2 * p.vs[2];
+  constexpr int RPI = 64 / CPR;
+  const int lrow = wave * RPI + lane / CPR;
+  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
+  const uint32_t k_voff = (uint32_t)(lrow * ksb + 16 * kchunk);
+  const uint32_t v_voff = (uint32_t)(lrow * vsb + 16 * kchunk);
+  auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int kv0) {
+    const uint32_t base = lds_address(buf) + 16 * 64 * wave;
+    if (kv0 + HB <= p.Skv) {
+      const char* g0 = g + kv0 * rsb;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16s(voff, g0 + 4 * RPI * i * rsb, base + 16 * 64 * 4 * i);
+    } else {
+      const int last = p.Skv - 1 - kv0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rr = min(lrow + 4 * RPI * i, last);
+        dma16(g + (kv0 + rr) * rsb + 16 * kchunk, base + 16 * 64 * 4 * i);
+      }
+    }
+  };
+  auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
+  auto issue = [&](int j) {
+    const int kv0 = kv0_of(j);
+    issue_one(Kp, ksb, k_lds[j % 2], k_voff, kv0);
+    issue_one(Vp, vsb, v_lds[j % 2], v_voff, kv0);
+  };
+  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
+
+  // ---- this lane's query row: Q and dO as B operands, its LSE and Delta ----
+  const int myq = q0 + wave * 32 + lq;
+  const bool q_ok = myq < p.Sq;
+  const int qc = q_ok ? myq : p.Sq - 1;
+  bf16x8_t qreg[KS], doreg[KS];
+  {
+    const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1] + (long long)qc * p.qs[2];
+    const uint16_t* Gp = P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1] + (long long)qc * P.dos[2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Qp + 16 * s + 8 * hh));
+      doreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Gp + 16 * s + 8 * hh));
+    }
+  }
+  const long long wrow = ((long long)b * p.Hq + hq) * P.sq_pad + myq;  // padded rows exist
+  const float lse2 = P.ws_lse2[wrow];      // +inf: the row attends nothing (P = 0)
+  const float delta = P.ws_delta[wrow];
+  const auto mrow = Mask::row(p.mask, b, hq, qc);
+  const auto srow = Score::row(p.score, b, hq, qc);
+
+  int koff[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = k_off(lq, 2 * s + hh);
+  // K^T operand (transposed reads, as the forward reads V^T): rows 4hh + si/4
+  // (+16 per k-step), lower and upper 8 rows, d block dt
+  int ktlo[DT], kthi[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
+    ktlo[dt] = k_off(4 * hh + (si >> 2), d >> 3) + (d & 7);
+    kthi[dt] = k_off(4 * hh + (si >> 2) + 8, d >> 3) + (d & 7);
+  }
+
+  f32x16_t dq[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) dq[i] = f32x16_t{};
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+  const int J = SPT * T;
+  if (J > 0) issue(0);
+  for (int j = 0; j < J; ++j) {
+    wait_vmcnt<0>();
+    wait_lds_reads();
+    __syncthreads();  // sub-tile j landed for every wave; every wave is done with j-1
+    if (j + 1 < J) issue(j + 1);
+    const int t = j / SPT;
+    const int kvt0 = kb_of(t) * kBN + HB * (j % SPT);
+    const bool partial = t < n_part;
+    const bool ragged = kvt0 + HB > p.Skv;
+    const uint32_t kbase = lds_address(k_lds[j % 2]), vbase = lds_address(v_lds[j % 2]);
+
+    // S^T = K Q^T and dP^T = V dO^T for this 64-key sub-tile
+    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int mt = i / KS, s = i % KS;
+      const bf16x8_t ak = *(const lds_bf16x8_t*)(uintptr_t)(kbase + 2 * (koff[s] + mt * 32 * D));
+      const bf16x8_t av = *(const lds_bf16x8_t*)(uintptr_t)(vbase + 2 * (koff[s] + mt * 32 * D));
+      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[mt], 0, 0, 0);
+      dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], dpacc[mt], 0, 0, 0);
+    }
+
+    // dS^T = P (dP - Delta) mod'(S); element (mt, r) is key kvb + cr
+    const int kvb = kvt0 + 4 * hh;
+    const int lim = ragged ? p.Skv - kvb : HB;
+    const float m_ref = lse2;
+    const auto st = Score::tile(srow, kvb, m_ref);
+    const auto mtl = Mask::tile(mrow, kvb);
+    bf16x8_t dsb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int mt = g >> 1, h8 = 8 * (g & 1);
+      bf16x2_t pk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float dsv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = h8 + 2 * k + u;
+          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+          const int crs = min(cr, lim - 1);  // in-bounds key for functors that read memory
+          const float sv = sacc[mt][r];
+          bool keep = cr < lim;
+          if (partial) keep = keep && Mask::keep(mtl, crs);
+          const float pv = keep ? __builtin_amdgcn_exp2f(Score::apply(st, sv, Score::kReadsMemory ? crs : cr)) : 0.0f;
+          dsv[u] = pv * (dpacc[mt][r] - delta) * Score::dmod1(srow, sv, kvb + crs);
+        }
+        pk[k][0] = (__bf16)dsv[0];
+        pk[k][1] = (__bf16)dsv[1];
+      }
+      dsb[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      const int ks = i / DT, dt = i % DT;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4_t*)(uintptr_t)(kbase + 2 * (ktlo[dt] + ks * 16 * D)));
+      const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4_t*)(uintptr_t)(kbase + 2 * (kthi[dt] + ks * 16 * D)));
+      const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks], dq[dt], 0, 0, 0);
+    }
+  }
+
+  if (q_ok) {
+    const float sc = p.score.scale;
+    uint16_t* Gq = P.dq + (long long)b * P.dqs[0] + (long long)hq * P.dqs[1] + (long long)myq * P.dqs[2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(dq[dt][4 * g + i] * sc);
+        *(bf16x4_t*)(Gq + 32 * dt + 8 * g + 4 * hh) = o4;
+      }
+    }
+  }
+}
+
+// ---- bwd_dkdv ------------------------------------------------------------------------
+template <int D, class Mask, class Score>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams P) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int HB = 64;                 // query rows per sub-step
+  constexpr int SPT = kBM / HB;
+  constexpr int NI = HB * CPR / 64 / 4;
+  const FwdParams& p = P.f;
+  // Q and dO sub-tiles, row-major with the K chunk swizzle, 2-deep ring
+  __shared__ __align__(16) uint16_t q_lds[2][HB * D];
+  __shared__ __align__(16) uint16_t g_lds[2][HB * D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hh = lane >> 5;
+  const int gi = lane >> 4, si = lane & 15;
+
+  const int NK = (p.Skv + kBN - 1) / kBN;
+  const int total = NK * p.Hkv * p.B;
+  const int L = xcd_logical_id(blockIdx.x, total);
+  const int kb = L % NK;
+  const int bh = L / NK;
+  const int hkv = bh % p.Hkv, b = bh / p.Hkv;
+  const int k0 = kb * kBN;
+
+  // ---- this lane's key row: K and V as B operands ----
+  const int mykv = k0 + wave * 32 + lq;
+  const bool kv_ok = mykv < p.Skv;
+  const int kvc = kv_ok ? mykv : p.Skv - 1;
+  bf16x8_t kreg[KS], vreg[KS];
+  {
+    const uint16_t* Kr = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1] + (long long)kvc * p.ks[2];
+    const uint16_t* Vr = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1] + (long long)kvc * p.vs[2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Kr + 16 * s + 8 * hh));
+      vreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Vr + 16 * s + 8 * hh));
+    }
+  }
+
+  // ---- the query tiles to visit: for each head of the group, its column lists ----
+  const BlockMaskView& bm = p.bm;
+  auto col_counts = [&](int hq, int& np, int& nf) {
+    if (bm.dense) {
+      np = 0;
+      nf = bm.NQ;
+      return;
+    }
+    const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
+    const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
+    np = P.q_num[col];
+    nf = bm.separate_full ? P.full_q_num[col] : 0;
+  };
+  auto col_entry = [&](int hq, int np, int t) -> int {  // query tile of entry t
+    if (bm.dense) return t;
+    const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
+    const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
+    return t < np ? P.q_idx[col * bm.NQ + t] : P.full_q_idx[col * bm.NQ + (t - np)];
+  };
+  // sub-step j -> (query head, list entry, half); heads of the group in order
+  int Jtot = 0;
+  for (int g = 0; g < p.G; ++g) {
+    int np, nf;
+    col_counts(hkv * p.G + g, np, nf);
+    Jtot += SPT * (np + nf);
+  }
+  auto locate = [&](int j, int& hq, int& np, int& t, int& half) {
+    for (int g = 0; g < p.G; ++g) {
+      int nf;
+      hq = hkv * p.G + g;
+      col_counts(hq, np, nf);
+      const int n = SPT * (np + nf);
+      if (j < n) {
+        t = j / SPT;
+        half = j % SPT;
+        return;
+      }
+      j -= n;
+    }
+  };
+
+  constexpr int RPI = 64 / CPR;
+  const int lrow = wave * RPI + lane / CPR;
+  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
+  const long long qsb = 2 * p.qs[2], gsb = 2 * P.dos[2];
+  const uint32_t q_voff = (uint32_t)(lrow * qsb + 16 * kchunk);
+  const uint32_t g_voff = (uint32_t)(lrow * gsb + 16 * kchunk);
+  auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int r0) {
+    const uint32_t base = lds_address(buf) + 16 * 64 * wave;
+    if (r0 + HB <= p.Sq) {
+      const char* g0 = g + r0 * rsb;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16s(voff, g0 + 4 * RPI * i * rsb, base + 16 * 64 * 4 * i);
+    } else {
+      const int last = p.Sq - 1 - r0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rr = min(lrow + 4 * RPI * i, last);
+        dma16(g + (r0 + rr) * rsb + 16 * kchunk, base + 16 * 64 * 4 * i);
+      }
+    }
+  };
+  auto issue = [&](int j) {
+    int hq, np, t, half;
+    locate(j, hq, np, t, half);
+    const int r0 = col_entry(hq, np, t) * kBM + HB * half;
+    const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1]);
+    const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1]);
+    issue_one(Qh, qsb, q_lds[j % 2], q_voff, r0);
+    issue_one(Gh, gsb, g_lds[j % 2], g_voff, r0);
+  };
+  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
+  int aoff[KS];  // Q / dO rows as A operands: row lq (+32 per query block), chunk 2s + hh
+#pragma unroll
+  for (int s = 0; s < KS; ++s) aoff[s] = k_off(lq, 2 * s + hh);
+  int ttlo[DT], tthi[DT];  // Q^T / dO^T through transposed reads
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = 32 * dt + 16 * (gi & 1) + 4 * (si & 3);
+    ttlo[dt] = k_off(4 * hh + (si >> 2), d >> 3) + (d & 7);
+    tthi[dt] = k_off(4 * hh + (si >> 2) + 8, d >> 3) + (d & 7);
+  }
+  auto tr_read = [&](uint32_t base, int dt, int ks) {
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(uintptr_t)(base + 2 * (ttlo[dt] + ks * 16 * D)));
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(uintptr_t)(base + 2 * (tthi[dt] + ks * 16 * D)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x16_t dv[DT], dk[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) {
+    dv[i] = f32x16_t{};
+    dk[i] = f32x16_t{};
+  }
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+  if (Jtot > 0) issue(0);
+  for (int j = 0; j < Jtot; ++j) {
+    wait_vmcnt<0>();
+    wait_lds_reads();
+    __syncthreads();
+    if (j + 1 < Jtot) issue(j + 1);
+    int hq, np, t, half;
+    locate(j, hq, np, t, half);
+    const int qs0 = col_entry(hq, np, t) * kBM + HB * half;  // first query row of the sub-step
+    const bool partial = t < np;
+    const uint32_t qbase = lds_address(q_lds[j % 2]), gbase = lds_address(g_lds[j % 2]);
+
+    // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
+    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int mt = i / KS, s = i % KS;
+      const bf16x8_t aq = *(const lds_bf16x8_t*)(uintptr_t)(qbase + 2 * (aoff[s] + mt * 32 * D));
+      const bf16x8_t ag = *(const lds_bf16x8_t*)(uintptr_t)(gbase + 2 * (aoff[s] + mt * 32 * D));
+      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc[mt], 0, 0, 0);
+      dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vreg[s], dpacc[mt], 0, 0, 0);
+    }
+
+    // LSE and Delta of the 16 query rows of each block this lane holds: rows
+    // 8 (r / 4) + 4 hh + r % 4, four runs of four (padded rows exist)
+    const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + qs0 + 4 * hh;
+    f32x4_t lse4[2][4], del4[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lse4[mt][g] = *(const f32x4_t*)(P.ws_lse2 + w0 + 32 * mt + 8 * g);
+        del4[mt][g] = *(const f32x4_t*)(P.ws_delta + w0 + 32 * mt + 8 * g);
+      }
+
+    // P and dS = P (dP - Delta) mod'(S), packed as bf16 B operands (k = query row)
+    bf16x8_t pb[4], dsb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int mt = g >> 1, h8 = 8 * (g & 1);
+      bf16x2_t pp[4], pd[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = h8 + 2 * k + u;
+          const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int qcl = min(q, p.Sq - 1);
+          const float sv = sacc[mt][r];
+          const auto srow = Score::row(p.score, b, hq, qcl);
+          bool keep = kv_ok && q < p.Sq;
+          if (partial) keep = keep && Mask::row(p.mask, b, hq, qcl)(kvc);
+          const float x2 = Score::apply1(srow, sv, kvc, 0);
+          const float pv = keep ? __builtin_amdgcn_exp2f(x2 - lse4[mt][r >> 2][r & 3]) : 0.0f;
+          const float dsv = pv * (dpacc[mt][r] - del4[mt][r >> 2][r & 3]) * Score::dmod1(srow, sv, kvc);
+          pp[k][u] = (__bf16)pv;
+          pd[k][u] = (__bf16)dsv;
+        }
+      }
+      pb[g] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      dsb[g] = __builtin_shufflevector(__builtin_shufflevector(pd[0], pd[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pd[2], pd[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (k = the 16 query rows of step ks)
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      const int ks = i / DT, dt = i % DT;
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gbase, dt, ks), pb[ks], dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qbase, dt, ks), dsb[ks], dk[dt], 0, 0, 0);
+    }
+  }
+
+  if (kv_ok) {
+    const float sc = p.score.scale;
+    uint16_t* Gk = P.dk + (long long)b * P.dks[0] + (long long)hkv * P.dks[1] + (long long)mykv * P.dks[2];
+    uint16_t* Gv = P.dv + (long long)b * P.dvs[0] + (long long)hkv * P.dvs[1] + (long long)mykv * P.dvs[2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t k4, v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k4[i] = (__bf16)(dk[dt][4 * g + i] * sc);
+          v4[i] = (__bf16)dv[dt][4 * g + i];
+        }
+        *(bf16x4_t*)(Gk + 32 * dt + 8 * g + 4 * hh) = k4;
+        *(bf16x4_t*)(Gv + 32 * dt + 8 * g + 4 * hh) = v4;
+      }
+    }
+  }
+}
+
+template <int D, class Mask>
+struct LaunchBwd {
+  const BwdParams& P;
+  hipStream_t stream;
+  template <class Score>
+  void operator()() {
+    const FwdParams& p = P.f;
+    const int NQ = (p.Sq + kBM - 1) / kBM, NK = (p.Skv + kBN - 1) / kBN;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, Mask, Score>), dim3((unsigned)(NQ * p.Hq * p.B)), dim3(kBwdThreads), 0,
+                       stream, P);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, Mask, Score>), dim3((unsigned)(NK * p.Hkv * p.B)),
+                       dim3(kBwdThreads), 0, stream, P);
+  }
+};
+
+// Launches the backward (after the prep kernel) for one mask kind, every score kind and both D.
+template <class Mask>
+fa_status launch_backward_mask(int D, int score_kind, const BwdParams& P, hipStream_t stream) {
+  bool ok;
+  if (D == 128) {
+    LaunchBwd<128, Mask> l{P, stream};
+    ok = dispatch_score(score_kind, l);
+  } else if (D == 64) {
+    LaunchBwd<64, Mask> l{P, stream};
+    ok = dispatch_score(score_kind, l);
+  } else {
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (!ok) return FA_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace fa

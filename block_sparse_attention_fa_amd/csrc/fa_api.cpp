@@ -219,7 +219,56 @@ fa_status prepare_decode(const fa_attn_args* a, FwdParams& p, int& mask_kind, De
   return FA_OK;
 }
 
+fa_status prepare_backward(const fa_attn_args* a, const fa_grad_args* g, BwdParams& P, int& mask_kind,
+                           size_t& bytes) {
+  fa_status st = prepare(a, false, P.f, mask_kind);
+  if (st != FA_OK) return st;
+  if (a->lse == nullptr) return fail(FA_ERR_NULL, "the backward needs the forward's LSE (lse)");
+  const fa_block_mask* bm = a->block_mask;
+  if (bm != nullptr && (!bm->q_num_blocks || !bm->q_indices || !bm->full_q_num_blocks || !bm->full_q_indices))
+    return fail(FA_ERR_NULL, "the backward needs the BlockMask's transposed view (q_num_blocks, q_indices, "
+                             "full_q_num_blocks, full_q_indices)");
+  const int NQ = ceil_div(a->Sq, FA_BLOCK);
+  P.sq_pad = NQ * FA_BLOCK;
+  bytes = 2 * sizeof(float) * (size_t)a->B * a->Hq * P.sq_pad;
+  if (g == nullptr) return FA_OK;  // size query
+  if (!g->dout || !g->dq || !g->dk || !g->dv) return fail(FA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
+  if ((st = check_strides("dout", g->dout_stride, g->dout)) != FA_OK) return st;
+  if ((st = check_strides("dq", g->dq_stride, g->dq)) != FA_OK) return st;
+  if ((st = check_strides("dk", g->dk_stride, g->dk)) != FA_OK) return st;
+  if ((st = check_strides("dv", g->dv_stride, g->dv)) != FA_OK) return st;
+  P.dout = g->dout;
+  P.dq = g->dq;
+  P.dk = g->dk;
+  P.dv = g->dv;
+  for (int i = 0; i < 4; ++i) {
+    P.dos[i] = g->dout_stride[i];
+    P.dqs[i] = g->dq_stride[i];
+    P.dks[i] = g->dk_stride[i];
+    P.dvs[i] = g->dv_stride[i];
+  }
+  P.q_num = bm ? bm->q_num_blocks : nullptr;
+  P.q_idx = bm ? bm->q_indices : nullptr;
+  P.full_q_num = bm ? bm->full_q_num_blocks : nullptr;
+  P.full_q_idx = bm ? bm->full_q_indices : nullptr;
+  return FA_OK;
+}
+
 }  // namespace
+
+fa_status launch_backward(int D, int mask_kind, int score_kind, const BwdParams& p, hipStream_t s) {
+  switch (mask_kind) {
+    case FA_MASK_NONE: return launch_backward_none(D, score_kind, p, s);
+    case FA_MASK_CAUSAL: return launch_backward_causal(D, score_kind, p, s);
+    case FA_MASK_SLIDING_WINDOW: return launch_backward_window(D, score_kind, p, s);
+    case FA_MASK_SLIDING_CAUSAL: return launch_backward_sliding_causal(D, score_kind, p, s);
+    case FA_MASK_DOCUMENT: return launch_backward_document(D, score_kind, p, s);
+    case FA_MASK_DOCUMENT_CAUSAL: return launch_backward_document_causal(D, score_kind, p, s);
+    case FA_MASK_PREFIX_LM: return launch_backward_prefix_lm(D, score_kind, p, s);
+    case FA_MASK_KV_LEN: return launch_backward_kv_len(D, score_kind, p, s);
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
 
 fa_status launch_forward(int D, int mask_kind, int score_kind, const FwdParams& p, hipStream_t s) {
   switch (mask_kind) {
@@ -352,6 +401,34 @@ fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_byt
   P.num_pages = a->num_pages;
   st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, (hipStream_t)stream);
   if (st != FA_OK) return fail(st, "decode launch failed");
+  return FA_OK;
+}
+
+fa_status fa_backward_workspace_size(const fa_attn_args* a, size_t* bytes) {
+  if (bytes == nullptr) return fail(FA_ERR_NULL, "bytes is NULL");
+  BwdParams P;
+  int mask_kind;
+  return prepare_backward(a, nullptr, P, mask_kind, *bytes);
+}
+
+fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (g == nullptr) return fail(FA_ERR_NULL, "gradient args are NULL");
+  BwdParams P;
+  int mask_kind;
+  size_t need;
+  fa_status st = prepare_backward(a, g, P, mask_kind, need);
+  if (st != FA_OK) return st;
+  if (workspace == nullptr) return fail(FA_ERR_WORKSPACE, "backward workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "backward workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 15u) != 0) return fail(FA_ERR_WORKSPACE, "backward workspace not 16-byte aligned");
+  P.ws_lse2 = (float*)workspace;
+  P.ws_delta = P.ws_lse2 + (size_t)a->B * a->Hq * P.sq_pad;
+  st = launch_backward_prep(a->D, P, (hipStream_t)stream);
+  if (st != FA_OK) return fail(st, "backward prep launch failed");
+  st = launch_backward(a->D, mask_kind, a->score.kind, P, (hipStream_t)stream);
+  if (st != FA_OK) return fail(st, "backward launch failed");
   return FA_OK;
 }
 

@@ -67,6 +67,23 @@ struct DecodeParams {
   int num_pages;
 };
 
+struct BwdParams {
+  FwdParams f;            // q, k, v, o (the forward's output), lse (its natural-log LSE), masks, scores
+  const uint16_t* dout;   // dO [B, Hq, Sq, D]
+  long long dos[4];
+  uint16_t* dq;           // outputs, bf16
+  uint16_t* dk;
+  uint16_t* dv;
+  long long dqs[4], dks[4], dvs[4];
+  const int* q_num;       // transposed BlockMask view (nullptr for dense)
+  const int* q_idx;
+  const int* full_q_num;
+  const int* full_q_idx;
+  float* ws_lse2;         // [B, Hq, sq_pad] base-2 LSE, +inf for rows without keys
+  float* ws_delta;        // [B, Hq, sq_pad] rowsum(dO * O)
+  int sq_pad;             // Sq rounded up to whole 128-row tiles
+};
+
 struct BuildParams {
   int* kv_num;
   int* kv_idx;
@@ -93,5 +110,15 @@ fa_status launch_forward_document_causal(int D, int score_kind, const FwdParams&
 fa_status launch_forward_prefix_lm(int D, int score_kind, const FwdParams& p, hipStream_t stream);
 fa_status launch_forward_kv_len(int D, int score_kind, const FwdParams& p, hipStream_t stream);
 fa_status launch_decode(int D, int G, int score_kind, const DecodeParams& p, hipStream_t stream);
+fa_status launch_backward(int D, int mask_kind, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_prep(int D, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_none(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_causal(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_window(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_sliding_causal(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_document(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_document_causal(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_prefix_lm(int D, int score_kind, const BwdParams& p, hipStream_t stream);
+fa_status launch_backward_kv_len(int D, int score_kind, const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

@@ -299,6 +299,8 @@ struct ScoreNone {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int, float m_ref) { return {r.c, -m_ref}; }
   static __device__ __forceinline__ float apply(const Tile& t, float s, int) { return fmaf(s, t.c, t.add); }
+  // d mod / d (scaled score), for the backward: 1 for every additive mod
+  static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
 // Concepts "score_mod": s + slope[h] * (kv - q).
@@ -326,6 +328,7 @@ struct ScoreAlibi {
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(t.sl, (float)cr, t.add));
   }
+  static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
 // Softcapping (paper review §2.1 table): cap * tanh(s / cap), with
@@ -355,6 +358,11 @@ struct ScoreSoftcap {
     const float e = __builtin_amdgcn_exp2f(s * t.k);
     return fmaf(t.neg2c2, __builtin_amdgcn_rcpf(1.0f + e), t.add);
   }
+  // d (cap tanh(x / cap)) / dx = 1 - tanh^2, with the same tanh as above
+  static __device__ __forceinline__ float dmod1(const Row& r, float s, int) {
+    const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * r.k));
+    return fmaf(-th, th, 1.0f);
+  }
 };
 
 // Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
@@ -378,6 +386,7 @@ struct ScoreRelPos {
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(-kLog2e, (float)cr, t.add));
   }
+  static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
 // Dynamic-bias feature request (attention-gym issue 123): s + bias[b,h,q,kv].
@@ -404,6 +413,7 @@ struct ScoreBias {
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(kLog2e, bf16_bits_to_float(t.row[cr]), t.add));
   }
+  static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
 // The dynamic bias with the forward staging each step's [128 query x 64 key]

@@ -65,6 +65,12 @@ class AttnArgs(ctypes.Structure):
                 ("page_table", c_void_p), ("page_table_stride", c_int64), ("num_pages", c_int32)]
 
 
+class GradArgs(ctypes.Structure):
+    _fields_ = [("dout", c_void_p), ("dout_stride", c_int64 * 4),
+                ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p),
+                ("dq_stride", c_int64 * 4), ("dk_stride", c_int64 * 4), ("dv_stride", c_int64 * 4)]
+
+
 # symbol -> (restype, argtypes)
 SIGNATURES = {
     "fa_abi_version": (c_int32, []),
@@ -75,6 +81,8 @@ SIGNATURES = {
     "fa_forward": (c_int32, [POINTER(AttnArgs), c_void_p]),
     "fa_decode_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
     "fa_decode": (c_int32, [POINTER(AttnArgs), c_void_p, c_size_t, c_void_p]),
+    "fa_backward_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
+    "fa_backward": (c_int32, [POINTER(AttnArgs), POINTER(GradArgs), c_void_p, c_size_t, c_void_p]),
 }
 
 
@@ -346,3 +354,43 @@ def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: S
     _check(lib().fa_decode(ctypes.byref(a), c_void_p(workspace.data_ptr()),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def fa_backward_workspace_size(q, k, v, out, lse, block_mask=None, score=None):
+    a = _attn_args(q, k, v, out, lse, block_mask, score, 0.0, 0)
+    n = c_size_t()
+    _check(lib().fa_backward_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+def fa_backward(q, k, v, out, lse, dout, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
+                scale=0.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fa_forward(q, k, v, ...) for the upstream gradient dout.
+
+    out and lse are what fa_forward returned for the same arguments; a
+    BlockMask must have been built with transposed=True.  Returns (dq, dk, dv)."""
+    import torch
+    if block_mask is not None and not block_mask.transposed:
+        raise FAError(FA_ERR_NULL, "the backward needs a BlockMask built with transposed=True")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(ref.shape) or not t.is_cuda:
+            raise FAError(FA_ERR_SHAPE, f"{name} must be a torch.bfloat16 GPU tensor shaped {tuple(ref.shape)}")
+    if lse is None:
+        raise FAError(FA_ERR_NULL, "the backward needs the forward's lse")
+    a = _attn_args(q, k, v, out, lse, block_mask, score, scale, 0)
+    g = GradArgs()
+    g.dout, g.dq, g.dk, g.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    for name, t in (("dout_stride", dout), ("dq_stride", dq), ("dk_stride", dk), ("dv_stride", dv)):
+        arr = getattr(g, name)
+        for i, st in enumerate(t.stride()):
+            arr[i] = st
+    n = c_size_t()
+    _check(lib().fa_backward_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(4, n.value // 4), dtype=torch.float32, device=q.device)
+    _check(lib().fa_backward(ctypes.byref(a), ctypes.byref(g), c_void_p(workspace.data_ptr()),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv

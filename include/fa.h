@@ -169,6 +169,18 @@ typedef struct {
   int32_t num_pages;          /* pages in each pool */
 } fa_attn_args;
 
+/* Backward pass: the gradient buffers.  Strides are in elements for (b, h, s, d),
+ * with the same rules as the forward's tensors (d stride 1, others multiples of 8,
+ * 16-byte aligned bases). */
+typedef struct {
+  const uint16_t* dout;       /* dO, bf16 [B,Hq,Sq,D]: the gradient of the loss at O */
+  int64_t dout_stride[4];
+  uint16_t* dq;               /* written: bf16 [B,Hq,Sq,D] */
+  uint16_t* dk;               /* written: bf16 [B,Hkv,Skv,D] (summed over the GQA group) */
+  uint16_t* dv;               /* written: bf16 [B,Hkv,Skv,D] */
+  int64_t dq_stride[4], dk_stride[4], dv_stride[4];
+} fa_grad_args;
+
 /* Version of this ABI (FA_ABI_VERSION). */
 int32_t fa_abi_version(void);
 
@@ -226,6 +238,30 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
  * Errors: as fa_forward, plus FA_ERR_SHAPE for Sq != 1, num_pages <= 0 or
  * page_table_stride < ceil(Skv / FA_BLOCK), and FA_ERR_WORKSPACE. */
 fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only.  Bytes of workspace fa_backward needs: two fp32 values (base-2
+ * LSE and Delta = rowsum(dO * O)) per query row, rows padded to whole tiles.
+ * Same validation as fa_backward. */
+fa_status fa_backward_workspace_size(const fa_attn_args* a, size_t* bytes);
+
+/* Backward pass (dQ, dK, dV) of fa_forward for the same arguments: the
+ * gradient of the forward definition, O = softmax(mod(Q K^T * scale)) V with
+ * the mask.  The pages name a backward pass that walks the transposed
+ * BlockMask view (Concepts "Key attributes": q_num_blocks / q_indices, "used in
+ * backward") without giving its formulas; with P recomputed from the forward's
+ * LSE, Delta = rowsum(dO * O), dS = P * (dP - Delta) * mod'(S) and dP = dO V^T:
+ * dV = P^T dO, dQ = scale * dS K, dK = scale * dS^T Q.  For the bias score the
+ * bias is an input, not a learned parameter: no bias gradient is produced.
+ * a->o must hold fa_forward's output and a->lse its LSE (both required).  A
+ * BlockMask must carry its transposed view (all four q_* buffers, built by
+ * fa_build_block_mask); NULL means dense.  No page table.
+ * Kernels: a prep kernel (LSE, Delta), a query-parallel dQ kernel walking the
+ * row lists and a key-parallel dK/dV kernel walking the column lists of every
+ * query head of the GQA group; no atomics.
+ * Errors: as fa_forward, plus FA_ERR_NULL (o, lse, dO, dQ, dK, dV or the
+ * transposed view missing) and FA_ERR_WORKSPACE. */
+fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,79 @@
+"""Backward (dQ, dK, dV) vs the fp64 oracle's gradients, element by element, for
+every mask_mod x score_mod at sizes that span several tiles and a ragged tail,
+both head dims, GQA, per-head and superset BlockMasks and the dense path.
+
+Tolerance (bf16 inputs and outputs, fp32 accumulation; P and dS are rounded to
+bf16 for the MFMAs, which is what bounds the error): per tensor, max abs error
+<= 2e-2 * max|ref| + 2e-3 and relative Frobenius error <= 1e-2.
+"""
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_fa_amd import inputs as gen
+from oracle import flex_oracle as fo
+from tests import _cases as C
+
+pytestmark = pytest.mark.gpu
+
+BATCH_DEP = ("document", "document_causal", "kv_len")
+TOL_REL_MAX = 2e-2
+TOL_ABS = 2e-3
+TOL_FRO = 1e-2
+
+
+def compare_grad(got, ref, what):
+    got = got.astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    err = np.abs(got - ref)
+    scale = float(np.abs(ref).max())
+    fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"[{what}] max abs {err.max():.3e} (ref max {scale:.3e}), rel fro {fro:.3e}", flush=True)
+    assert err.max() <= TOL_REL_MAX * scale + TOL_ABS, f"{what}: max abs err {err.max():.3e}, ref max {scale:.3e}"
+    assert fro <= TOL_FRO or scale == 0.0, f"{what}: relative Frobenius error {fro:.3e}"
+
+
+def run_bwd(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense=False, per_head=False,
+            scale=0.0, **kw):
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    print(f"[case] bwd seed={seed} mask={mask} score={score} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} "
+          f"sep={separate_full} dense={dense} per_head={per_head}", flush=True)
+    q, k, v = gen.qkv(seed, B, Hq, Hkv, Sq, Skv, D)
+    dO = gen._normal_bf16([seed, 30], (B, Hq, Sq, D), 1.0)
+    spec = C.make_spec(seed, mask, score, B, Hq, Sq, Skv, **kw)
+    qt, kt, vt, dOt = (gen.to_torch_bf16(x) for x in (q, k, v, dO))
+    bm = None
+    if not dense:
+        Bm = B if mask in BATCH_DEP else 1
+        Hm = Hq if per_head else 1
+        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True)
+    sc = C.gpu_score(spec)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=sc, lse=lse, scale=scale)
+    dq, dk, dv = fa.fa_backward(qt, kt, vt, out, lse, dOt, block_mask=bm, score=sc, scale=scale)
+    torch.cuda.synchronize()
+    refs = fo.attention_backward(q, k, v, dO, None if dense else C.oracle_mask(spec), C.oracle_score(spec, Hq),
+                                 scale=scale if scale > 0 else None)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        compare_grad(gen.bf16_bits_to_f32(gen.from_torch_bf16(g)), r, f"{name} {mask}/{score} D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("score", C.SCORE_NAMES)
+@pytest.mark.parametrize("mask", ["none", "causal", "sliding_causal", "document_causal", "prefix_lm", "kv_len"])
+def test_backward_mask_score_matrix(mask, score, D):
+    run_bwd(51, mask, score, 2, 4, 2, 300, 300, D)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (129, 129)])
+@pytest.mark.parametrize("mask", ["causal", "kv_len", "none"])
+def test_backward_uneven_lengths(mask, Sq, Skv):
+    run_bwd(52, mask, "alibi", 2, 2, 2, Sq, Skv, 128)
+
+
+def test_backward_superset_dense_per_head_and_scale():
+    run_bwd(53, "causal", "softcap", 1, 4, 2, 260, 260, 128, separate_full=False)
+    run_bwd(54, "none", "alibi", 1, 4, 1, 200, 200, 64, dense=True)
+    run_bwd(55, "sliding_causal", "none", 1, 4, 4, 300, 300, 128, per_head=True)
+    run_bwd(56, "causal", "rel_pos", 2, 8, 1, 160, 160, 128, scale=0.05)
