@@ -165,6 +165,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="only time the block-skipping ablation and the sliding-window sparsity sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -274,6 +275,40 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "kernel": "fwd_kernel<128, MaskCausal, ScoreAlibi>"},
     }
+
+    # ---------------- backward of the same workload ----------------
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        bmt = fa.fa_build_block_mask(mask, 1, 1, S, S, device=dev, transposed=True)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+        fa.fa_forward(qt, kt, vt, block_mask=bmt, score=score, out=out, lse=lse)
+        dot = gen.to_torch_bf16(gen._normal_bf16([FWD["workload_id"], 30], (B, H, S, D)), dev)
+        dq, dk, dv = torch.empty_like(qt), torch.empty_like(kt), torch.empty_like(vt)
+        wsb = torch.empty(fa.fa_backward_workspace_size(qt, kt, vt, out, lse, bmt, score) // 4 + 4,
+                          dtype=torch.float32, device=dev)
+
+        def bwd():
+            fa.fa_backward(qt, kt, vt, out, lse, dot, block_mask=bmt, score=score, dq=dq, dk=dk, dv=dv,
+                           workspace=wsb)
+
+        bwd_settle, bwd_steps = 5, 10  # ~10 ms per call: 5 calls settle the clock
+        for _ in range(bwd_settle):
+            bwd()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(bwd_steps):
+            bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / bwd_steps
+        bwd_tflops = 10.0 * D * n_att / (bwd_ms * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": "backward of " + FWD["name"], "ms": round(bwd_ms, 4),
+            "attended_tflops": round(bwd_tflops, 2), "frac_bf16_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "flops_per_attended_position": "10*D (S, dP, dV, dK, dQ products)",
+            "kernels": "bwd_prep + bwd_dq_kernel + bwd_dkdv_kernel", "untimed_calls": bwd_settle,
+            "timed_calls": bwd_steps}
+        del dot, dq, dk, dv, wsb, lse
     del qt, kt, vt, out
     torch.cuda.empty_cache()
 

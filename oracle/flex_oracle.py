@@ -338,6 +338,76 @@ def attention_backward(q, k, v, dout, mask_mod=None, score_mod=None, scale=None)
     return dQ, dK, dV
 
 
+def _kept_scores(q, k, b, hq, rows, kv_rows, mask_mod, score_mod, scale):
+    """Mask, scaled scores S, S' = mod(S) (-inf where masked) and mod'(S) for a
+    block of (query rows x key rows) of (b, hq), as in attention_backward."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    hkv = hq // (Hq // Hkv)
+    Q, K = _values(q[b, hq, rows]), _values(k[b, hkv, kv_rows])
+    S = scale * (Q @ K.T)
+    qi, ki = np.asarray(rows)[:, None], np.asarray(kv_rows)[None, :]
+    M = np.ones(S.shape, dtype=bool) if mask_mod is None else \
+        np.broadcast_to(np.asarray(mask_mod(b, hq, qi, ki), dtype=bool), S.shape)
+    qb, kb = np.broadcast_arrays(qi, ki)
+    Sp, dmod = np.full_like(S, NEG_INF), np.zeros_like(S)
+    if score_mod is None:
+        Sp[M], dmod[M] = S[M], 1.0
+    else:
+        args = (S[M], b, hq, qb[M], kb[M])
+        Sp[M], dmod[M] = score_mod(*args), score_mod.grad(*args)
+    return Sp, dmod
+
+
+def attention_backward_q_rows(q, k, v, dout, b, hq, rows, mask_mod=None, score_mod=None, scale=None):
+    """dQ of query rows `rows` of (b, hq) alone: a row's dQ depends only on that
+    row (its softmax, dP = dO V^T and Delta), so sampled rows of a large problem
+    cost one row of work each.  Same steps as attention_backward."""
+    D, Skv = q.shape[3], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    hkv = hq // (q.shape[1] // k.shape[1])
+    rows = np.asarray(rows, dtype=np.int64)
+    Sp, dmod = _kept_scores(q, k, b, hq, rows, np.arange(Skv), mask_mod, score_mod, scale)
+    m = Sp.max(axis=1)
+    P = np.zeros_like(Sp)
+    live = m > NEG_INF
+    E = np.exp(Sp[live] - m[live, None])
+    P[live] = E / E.sum(axis=1)[:, None]
+    dP = _values(dout[b, hq, rows]) @ _values(v[b, hkv]).T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True)) * dmod
+    return scale * (dS @ _values(k[b, hkv]))
+
+
+def attention_backward_kv_rows(q, k, v, dout, b, hkv, kv_rows, mask_mod=None, score_mod=None, scale=None,
+                               chunk=1024):
+    """dK and dV of key rows `kv_rows` of (b, hkv), summed over the query heads of
+    its group.  A key row's gradient needs P[q, kv] for every query row, i.e.
+    every row's softmax normaliser, so each row's log-sum-exp is computed here
+    first (attention_rows over all keys); then, per query head and row chunk,
+    the same steps as attention_backward restricted to these key columns."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    kv_rows = np.asarray(kv_rows, dtype=np.int64)
+    dK = np.zeros((kv_rows.size, D))
+    dV = np.zeros((kv_rows.size, D))
+    V = _values(v[b, hkv])
+    for hq in range(hkv * (Hq // Hkv), (hkv + 1) * (Hq // Hkv)):
+        for r0 in range(0, Sq, chunk):
+            rows = np.arange(r0, min(Sq, r0 + chunk))
+            O, lse = attention_rows(q, k, v, b, hq, rows, mask_mod, score_mod, scale, check_rows_sum=False)
+            Sp, dmod = _kept_scores(q, k, b, hq, rows, kv_rows, mask_mod, score_mod, scale)
+            live = lse > NEG_INF
+            P = np.zeros_like(Sp)
+            P[live] = np.exp(Sp[live] - lse[live, None])
+            dO = _values(dout[b, hq, rows])
+            dP = dO @ V[kv_rows].T
+            delta = (dO * O).sum(axis=1, keepdims=True)    # rowsum(dO * O) = rowsum(P * dP) over all keys
+            dS = P * (dP - delta) * dmod
+            dV += P.T @ dO
+            dK += scale * (dS.T @ _values(q[b, hq, rows]))
+    return dK, dV
+
+
 # ---------------------------------------------------------------------------
 # BlockMask (Concepts "BlockMask Internals" / "Key attributes"; paper review §4.1-4.2)
 # ---------------------------------------------------------------------------

@@ -134,6 +134,42 @@ def test_document_causal_bias_B1_H32_S16384_D64():
     torch.cuda.empty_cache()
 
 
+def test_backward_causal_alibi_B4_H16_S8192_D128():
+    """dQ on sampled query rows and dK, dV on sampled key rows of the forward
+    workload, through fa_build_block_mask(transposed) + fa_forward + fa_backward."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, H, S, D = 4, 16, 8192, 128
+    print(f"[case] backward causal+alibi B{B} H{H} S{S} D{D}", flush=True)
+    q, k, v = gen.qkv(2, B, H, H, S, S, D)
+    dO = gen._normal_bf16([2, 30], (B, H, S, D), 1.0)
+    qt, kt, vt, dOt = (gen.to_torch_bf16(x) for x in (q, k, v, dO))
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, 1, S, S, transposed=True)
+    sc = fa.ScoreMod("alibi")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=sc, lse=lse)
+    dq, dk, dv = fa.fa_backward(qt, kt, vt, out, lse, dOt, block_mask=bm, score=sc)
+    torch.cuda.synchronize()
+    mask, score = fo.causal(), fo.alibi(fo.default_alibi_slopes(H))
+    rows = _sample_rows(2, S, 12)
+    got_q, ref_q = [], []
+    for b, h in _heads(2, B, H, 3):
+        got_q.append(gen.bf16_bits_to_f32(gen.from_torch_bf16(dq[b, h, torch.from_numpy(rows).cuda()])))
+        ref_q.append(fo.attention_backward_q_rows(q, k, v, dO, b, h, rows, mask, score))
+    C.compare_grad(np.concatenate(got_q), np.concatenate(ref_q), "dQ 8192 sampled rows")
+    kv_rows = np.array(sorted({0, 127, 128, 4095, S - 129, S - 1} | set(np.random.default_rng([2, 97]).integers(0, S, 4).tolist())))
+    got_k, got_v, ref_k, ref_v = [], [], [], []
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        idx = torch.from_numpy(kv_rows).cuda()
+        got_k.append(gen.bf16_bits_to_f32(gen.from_torch_bf16(dk[b, h, idx])))
+        got_v.append(gen.bf16_bits_to_f32(gen.from_torch_bf16(dv[b, h, idx])))
+        gk, gv = fo.attention_backward_kv_rows(q, k, v, dO, b, h, kv_rows, mask, score)
+        ref_k.append(gk)
+        ref_v.append(gv)
+    C.compare_grad(np.concatenate(got_k), np.concatenate(ref_k), "dK 8192 sampled rows")
+    C.compare_grad(np.concatenate(got_v), np.concatenate(ref_v), "dV 8192 sampled rows")
+
+
 def test_decode_B32_Hq32_Hkv8_KV32768_softcap50():
     import torch
     from block_sparse_attention_fa_amd import fa

@@ -633,3 +633,22 @@ def test_transposed_block_lists():
                 assert list(bm["q_indices"][0, 0, kb]) == rows + [0] * (NQ - len(rows))
                 assert bm["full_q_num_blocks"][0, 0, kb] == len(full)
                 assert list(bm["full_q_indices"][0, 0, kb]) == full + [0] * (NQ - len(full))
+
+
+def test_backward_row_and_column_samplers_match_the_full_backward():
+    """The sampled-row helpers used at full sizes give the full backward's rows."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 90, 16
+    q, k, v = gen.qkv(39, B, Hq, Hkv, S, S, D)
+    dO = gen._normal_bf16([39, 30], (B, Hq, S, D), 1.0)
+    docs = gen.document_ids(39, B, S, 10, 40)
+    for om, sm in ((fo.causal(), fo.alibi(fo.default_alibi_slopes(Hq))), (fo.document_causal(docs), fo.softcap(1.5)),
+                   (None, fo.rel_pos())):
+        dQ, dK, dV = fo.attention_backward(q, k, v, dO, om, sm)
+        rows = np.array([0, 5, 44, 89])
+        for b, hq in ((0, 0), (1, 3)):
+            np.testing.assert_allclose(fo.attention_backward_q_rows(q, k, v, dO, b, hq, rows, om, sm),
+                                       dQ[b, hq, rows], rtol=0, atol=1e-12)
+        for b, hkv in ((0, 1), (1, 0)):
+            gk, gv = fo.attention_backward_kv_rows(q, k, v, dO, b, hkv, rows, om, sm, chunk=32)
+            np.testing.assert_allclose(gk, dK[b, hkv, rows], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(gv, dV[b, hkv, rows], rtol=0, atol=1e-12)
