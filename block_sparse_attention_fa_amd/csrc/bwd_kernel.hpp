@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams P) {
 
 // ---- bwd_dq ----------------------------------------------------------------------
 template <int D, class Mask, class Score>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdParams P) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams P) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
@@ -336,26 +336,30 @@ void bwd_dkdv_kernel(BwdParams P) {
     const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
     return t < np ? P.q_idx[col * bm.NQ + t] : P.full_q_idx[col * bm.NQ + (t - np)];
   };
-  // sub-step j -> (query head, list entry, half); heads of the group in order
+  // sub-step j -> (query head, list entry, half); heads of the group in order.
+  // The list lengths of the group's heads (at most 8) are read once.
+  int cnt_p[8], cnt_n[8];
   int Jtot = 0;
-  for (int g = 0; g < p.G; ++g) {
-    int np, nf;
-    col_counts(hkv * p.G + g, np, nf);
-    Jtot += SPT * (np + nf);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    int np = 0, nf = 0;
+    if (g < p.G) col_counts(hkv * p.G + g, np, nf);
+    cnt_p[g] = np;
+    cnt_n[g] = SPT * (np + nf);
+    Jtot += cnt_n[g];
   }
   auto locate = [&](int j, int& hq, int& np, int& t, int& half) {
-    for (int g = 0; g < p.G; ++g) {
-      int nf;
-      hq = hkv * p.G + g;
-      col_counts(hq, np, nf);
-      const int n = SPT * (np + nf);
-      if (j < n) {
-        t = j / SPT;
-        half = j % SPT;
-        return;
+    int g = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i)
+      if (g == i && j >= cnt_n[i]) {
+        j -= cnt_n[i];
+        g = i + 1;
       }
-      j -= n;
-    }
+    hq = hkv * p.G + g;
+    np = cnt_p[g];
+    t = j / SPT;
+    half = j % SPT;
   };
 
   constexpr int RPI = 64 / CPR;
@@ -427,6 +431,18 @@ void bwd_dkdv_kernel(BwdParams P) {
     const int qs0 = col_entry(hq, np, t) * kBM + HB * half;  // first query row of the sub-step
     const bool partial = t < np;
     const uint32_t qbase = lds_address(q_lds[j % 2]), gbase = lds_address(g_lds[j % 2]);
+    // LSE and Delta of the 16 query rows of each block this lane holds: rows
+    // 8 (r / 4) + 4 hh + r % 4, four runs of four (padded rows exist); loaded
+    // here so they arrive while the MFMAs below run
+    const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + qs0 + 4 * hh;
+    f32x4_t lse4[2][4], del4[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lse4[mt][g] = *(const f32x4_t*)(P.ws_lse2 + w0 + 32 * mt + 8 * g);
+        del4[mt][g] = *(const f32x4_t*)(P.ws_delta + w0 + 32 * mt + 8 * g);
+      }
 
     // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
@@ -438,18 +454,6 @@ void bwd_dkdv_kernel(BwdParams P) {
       sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc[mt], 0, 0, 0);
       dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vreg[s], dpacc[mt], 0, 0, 0);
     }
-
-    // LSE and Delta of the 16 query rows of each block this lane holds: rows
-    // 8 (r / 4) + 4 hh + r % 4, four runs of four (padded rows exist)
-    const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + qs0 + 4 * hh;
-    f32x4_t lse4[2][4], del4[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lse4[mt][g] = *(const f32x4_t*)(P.ws_lse2 + w0 + 32 * mt + 8 * g);
-        del4[mt][g] = *(const f32x4_t*)(P.ws_delta + w0 + 32 * mt + 8 * g);
-      }
 
     // P and dS = P (dP - Delta) mod'(S), packed as bf16 B operands (k = query row)
     bf16x8_t pb[4], dsb[4];
