@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 
   // An iteration covers STEP consecutive rows of the chunk (inside one tile):
   // lane group rr of wave w holds rows u * RSTEP + w * RPW + rr, u < U.  The
-  // next iteration's rows are loaded while the current ones are used.
+  // next iteration's rows are loaded while the current ones are used.  Each
+  // K/V row is read once per call, so the loads are non-temporal (+5% here).
   constexpr int U = 4;
   constexpr int STEP = RSTEP * U;
   static_assert(FA_BLOCK % STEP == 0, "an iteration stays inside one tile");
@@ -161,9 +162,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
       u32x4_t v = {0u, 0u, 0u, 0u};
       if constexpr (PAGED) {  // row r0 + u RSTEP of the tile's page
         const uint16_t* Xt = X + (v_rows ? s_voff[t] : s_koff[t]);
-        if (kv < p.Skv) v = *(const u32x4_t*)(Xt + (long long)(r0 + u * RSTEP) * xs + 8 * sub);
+        if (kv < p.Skv) v = __builtin_nontemporal_load((const u32x4_t*)(Xt + (long long)(r0 + u * RSTEP) * xs + 8 * sub));
       } else {
-        if (kv < p.Skv) v = *(const u32x4_t*)(X + (long long)kv * xs + 8 * sub);
+        if (kv < p.Skv) v = __builtin_nontemporal_load((const u32x4_t*)(X + (long long)kv * xs + 8 * sub));
       }
       x[u] = v;
     }
