@@ -36,6 +36,19 @@ namespace fa {
 
 constexpr int kBwdThreads = 256;
 
+// LDS chunk swizzle for tiles that are read both by rows (ds_read_b128: 16
+// lanes = 16 consecutive rows, one 16-byte chunk) and transposed
+// (ds_read_b64_tr_b16: 32 lanes = 4 consecutive rows x 4 adjacent chunks).
+// Rows are 256 bytes (D = 128, one pass over the 64 banks) or 128 bytes
+// (D = 64, two rows per pass).  The swizzle is a bijection on the 16 rows of
+// a row read, and it maps the 4 x 4 chunks of a transposed read to 16
+// distinct bank groups, so neither read pattern has bank conflicts.  (The
+// forward's K and V swizzles each serve one of the two patterns.)
+template <int D>
+__device__ __forceinline__ int rt_swizzle(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 // ---- bwd_prep: Delta = rowsum(dO * O) and LSE * log2(e) per query row --------------
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams P) {
@@ -124,7 +137,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const long long ksb = 2 * p.ks[2], vsb = 2 * p.vs[2];
   constexpr int RPI = 64 / CPR;
   const int lrow = wave * RPI + lane / CPR;
-  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
+  const int kchunk = (lane % CPR) ^ rt_swizzle<D>(lrow);
   const uint32_t k_voff = (uint32_t)(lrow * ksb + 16 * kchunk);
   const uint32_t v_voff = (uint32_t)(lrow * vsb + 16 * kchunk);
   auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int kv0) {
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     issue_one(Kp, ksb, k_lds[j % 2], k_voff, kv0);
     issue_one(Vp, vsb, v_lds[j % 2], v_voff, kv0);
   };
-  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
+  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ rt_swizzle<D>(r)) * 8); };
 
   // ---- this lane's query row: Q and dO as B operands, its LSE and Delta ----
   const int myq = q0 + wave * 32 + lq;
@@ -364,7 +377,7 @@ void bwd_dkdv_kernel(BwdParams P) {
 
   constexpr int RPI = 64 / CPR;
   const int lrow = wave * RPI + lane / CPR;
-  const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
+  const int kchunk = (lane % CPR) ^ rt_swizzle<D>(lrow);
   const long long qsb = 2 * p.qs[2], gsb = 2 * P.dos[2];
   const uint32_t q_voff = (uint32_t)(lrow * qsb + 16 * kchunk);
   const uint32_t g_voff = (uint32_t)(lrow * gsb + 16 * kchunk);
@@ -392,7 +405,7 @@ void bwd_dkdv_kernel(BwdParams P) {
     issue_one(Qh, qsb, q_lds[j % 2], q_voff, r0);
     issue_one(Gh, gsb, g_lds[j % 2], g_voff, r0);
   };
-  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
+  auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ rt_swizzle<D>(r)) * 8); };
   int aoff[KS];  // Q / dO rows as A operands: row lq (+32 per query block), chunk 2s + hh
 #pragma unroll
   for (int s = 0; s < KS; ++s) aoff[s] = k_off(lq, 2 * s + hh);
