@@ -206,3 +206,31 @@ def test_transposed_view_is_all_or_nothing():
     c.mask = fa.MaskMod("causal").desc()
     c.q_num_blocks = c.q_indices = 0x20000      # two of the four
     assert fa.lib().fa_build_block_mask(ctypes.byref(c), 256, 256, None) == fa.FA_ERR_NULL
+
+
+def _rt_swizzle(D, r):
+    # restated from rt_swizzle in block_sparse_attention_fa_amd/csrc/bwd_kernel.hpp
+    return 4 * (r & 3) + ((r >> 2) & 3) if D == 128 else (((r >> 1) & 1) << 2) | ((r >> 2) & 3)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_lds_swizzle_is_conflict_free(D):
+    """The backward's tile swizzle: no LDS bank conflict for a row read (16 lanes,
+    16 consecutive rows, one 16-byte chunk) nor for a transposed read (32 lanes,
+    4 consecutive rows x 4 adjacent chunks), and one chunk per lane for all of a
+    wave's DMA rows.  64 banks x 4 bytes: a 16-byte chunk covers one of 16 bank
+    groups of a 256-byte bank row."""
+    cpr = D // 8
+
+    def group(r, c):
+        return ((r * D * 2 + 16 * (c ^ _rt_swizzle(D, r))) % 256) // 16
+
+    for r0 in range(0, 128, 16):
+        for c in range(cpr):
+            assert len({group(r0 + i, c) for i in range(16)}) == 16
+    for r0 in range(0, 128, 4):
+        for c0 in range(0, cpr, 4):
+            assert len({group(r0 + i, c0 + j) for i in range(4) for j in range(4)}) == 16
+    step = 16 if D == 128 else 32  # rows between the DMA loads of one lane
+    for lrow in range(64):
+        assert len({_rt_swizzle(D, lrow + step * i) for i in range(4)}) == 1
