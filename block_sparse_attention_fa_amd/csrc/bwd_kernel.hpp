@@ -298,9 +298,11 @@ void bwd_dkdv_kernel(BwdParams P) {
   constexpr int SPT = kBM / HB;
   constexpr int NI = HB * CPR / 64 / 4;
   const FwdParams& p = P.f;
-  // Q and dO sub-tiles, row-major with the K chunk swizzle, 2-deep ring
-  __shared__ __align__(16) uint16_t q_lds[2][HB * D];
-  __shared__ __align__(16) uint16_t g_lds[2][HB * D];
+  // Q and dO sub-tiles, row-major with the row/transposed swizzle, 3-deep ring:
+  // step j reads sub-tile j (S, dP) and j - 1 (the delayed dV, dK products)
+  // while sub-tile j + 1 loads
+  __shared__ __align__(16) uint16_t q_lds[3][HB * D];
+  __shared__ __align__(16) uint16_t g_lds[3][HB * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -318,6 +320,7 @@ void bwd_dkdv_kernel(BwdParams P) {
   // ---- this lane's key row: K and V as B operands ----
   const int mykv = k0 + wave * 32 + lq;
   const bool kv_ok = mykv < p.Skv;
+  const bool kv_all = k0 + kBN <= p.Skv;  // every key of the block exists
   const int kvc = kv_ok ? mykv : p.Skv - 1;
   bf16x8_t kreg[KS], vreg[KS];
   {
@@ -402,8 +405,8 @@ void bwd_dkdv_kernel(BwdParams P) {
     const int r0 = col_entry(hq, np, t) * kBM + HB * half;
     const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1]);
     const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1]);
-    issue_one(Qh, qsb, q_lds[j % 2], q_voff, r0);
-    issue_one(Gh, gsb, g_lds[j % 2], g_voff, r0);
+    issue_one(Qh, qsb, q_lds[j % 3], q_voff, r0);
+    issue_one(Gh, gsb, g_lds[j % 3], g_voff, r0);
   };
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ rt_swizzle<D>(r)) * 8); };
   int aoff[KS];  // Q / dO rows as A operands: row lq (+32 per query block), chunk 2s + hh
@@ -433,17 +436,40 @@ void bwd_dkdv_kernel(BwdParams P) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+  // Software pipeline: the element-wise work of sub-step j runs beside the
+  // dV / dK MFMAs of sub-step j - 1 (whose P and dS were kept), so the wave
+  // has independent MFMAs in flight while it computes P and dS.  Stage 2
+  // stands in for "sub-step -1" at j = 0: zeroed, with P = dS = 0.
+  {
+    u32x4_t* z0 = (u32x4_t*)q_lds[2];
+    u32x4_t* z1 = (u32x4_t*)g_lds[2];
+    for (int i = tid; i < HB * D / 8; i += kBwdThreads) z0[i] = z1[i] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  bf16x8_t pbo[4], dsbo[4];  // P and dS of the previous sub-step
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pbo[i] = dsbo[i] = bf16x8_t{};
+  auto dvdk_mfma = [&](uint32_t qb_prev, uint32_t gb_prev, int ks) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gb_prev, dt, ks), pbo[ks], dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb_prev, dt, ks), dsbo[ks], dk[dt], 0, 0, 0);
+    }
+  };
+
   if (Jtot > 0) issue(0);
   for (int j = 0; j < Jtot; ++j) {
     wait_vmcnt<0>();
     wait_lds_reads();
-    __syncthreads();
+    __syncthreads();  // sub-step j landed; every wave is done with j - 2, whose stage j + 1 reuses
     if (j + 1 < Jtot) issue(j + 1);
     int hq, np, t, half;
     locate(j, hq, np, t, half);
     const int qs0 = col_entry(hq, np, t) * kBM + HB * half;  // first query row of the sub-step
     const bool partial = t < np;
-    const uint32_t qbase = lds_address(q_lds[j % 2]), gbase = lds_address(g_lds[j % 2]);
+    const auto srow0 = Score::row(p.score, b, hq, 0);  // (before the MFMAs: it may branch)
+    const bool fix = partial | (qs0 + HB > p.Sq) | !kv_all;  // needs the zeroing pass below
+    const uint32_t qbase = lds_address(q_lds[j % 3]), gbase = lds_address(g_lds[j % 3]);
+    const uint32_t qprev = lds_address(q_lds[(j + 2) % 3]), gprev = lds_address(g_lds[(j + 2) % 3]);
     // LSE and Delta of the 16 query rows of each block this lane holds: rows
     // 8 (r / 4) + 4 hh + r % 4, four runs of four (padded rows exist); loaded
     // here so they arrive while the MFMAs below run
@@ -468,43 +494,55 @@ void bwd_dkdv_kernel(BwdParams P) {
       dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vreg[s], dpacc[mt], 0, 0, 0);
     }
 
-    // P and dS = P (dP - Delta) mod'(S), packed as bf16 B operands (k = query row)
-    bf16x8_t pb[4], dsb[4];
+    // P and dS = P (dP - Delta) mod'(S) of sub-step j, in place of S and dP,
+    // with one MFMA of dV^T += dO^T P or dK^T += Q^T dS of sub-step j - 1 after
+    // every 32 / (8 DT) elements.  Element (mt, r): query row
+    // qs0 + 32 mt + 8 (r / 4) + 4 hh + r % 4 of this lane's key.
+    constexpr int EPM = 32 / (8 * DT);  // elements per MFMA
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int mt = e >> 4, r = e & 15;
+      const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float sv = sacc[mt][r];
+      const auto srow = Score::at(p.score, srow0, min(q, p.Sq - 1));
+      const float pv = __builtin_amdgcn_exp2f(Score::apply1(srow, sv, kvc, 0) - lse4[mt][r >> 2][r & 3]);
+      dpacc[mt][r] = pv * (dpacc[mt][r] - del4[mt][r >> 2][r & 3]) * Score::dmod1(srow, sv, kvc);
+      sacc[mt][r] = pv;
+      if (e % EPM == EPM - 1) {
+        const int i = e / EPM, ks = i / (2 * DT), dt = (i >> 1) % DT;
+        if (i & 1)
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qprev, dt, ks), dsbo[ks], dk[dt], 0, 0, 0);
+        else
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gprev, dt, ks), pbo[ks], dv[dt], 0, 0, 0);
+      }
+    }
+    // Zero what the mask drops (partial tiles), rows past Sq and a key past Skv
+    if (fix) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int mt = e >> 4, r = e & 15;
+        const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        bool keep = kv_ok && q < p.Sq;
+        if (partial) keep = keep && Mask::row(p.mask, b, hq, min(q, p.Sq - 1))(kvc);
+        sacc[mt][r] = keep ? sacc[mt][r] : 0.0f;
+        dpacc[mt][r] = keep ? dpacc[mt][r] : 0.0f;
+      }
+    }
+    // packed as bf16 B operands (k = query row): k-step g holds elements 8 g .. 8 g + 7
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int mt = g >> 1, h8 = 8 * (g & 1);
-      bf16x2_t pp[4], pd[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = h8 + 2 * k + u;
-          const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int qcl = min(q, p.Sq - 1);
-          const float sv = sacc[mt][r];
-          const auto srow = Score::row(p.score, b, hq, qcl);
-          bool keep = kv_ok && q < p.Sq;
-          if (partial) keep = keep && Mask::row(p.mask, b, hq, qcl)(kvc);
-          const float x2 = Score::apply1(srow, sv, kvc, 0);
-          const float pv = keep ? __builtin_amdgcn_exp2f(x2 - lse4[mt][r >> 2][r & 3]) : 0.0f;
-          const float dsv = pv * (dpacc[mt][r] - del4[mt][r >> 2][r & 3]) * Score::dmod1(srow, sv, kvc);
-          pp[k][u] = (__bf16)pv;
-          pd[k][u] = (__bf16)dsv;
-        }
+      for (int k = 0; k < 8; ++k) {
+        pbo[g][k] = (__bf16)sacc[mt][h8 + k];
+        dsbo[g][k] = (__bf16)dpacc[mt][h8 + k];
       }
-      pb[g] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-      dsb[g] = __builtin_shufflevector(__builtin_shufflevector(pd[0], pd[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(pd[2], pd[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     }
-
-    // dV^T += dO^T P and dK^T += Q^T dS (k = the 16 query rows of step ks)
+  }
+  if (Jtot > 0) {  // the last sub-step's dV / dK (its stage is still intact)
+    const uint32_t ql = lds_address(q_lds[(Jtot - 1) % 3]), gl = lds_address(g_lds[(Jtot - 1) % 3]);
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
-      const int ks = i / DT, dt = i % DT;
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gbase, dt, ks), pb[ks], dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qbase, dt, ks), dsb[ks], dk[dt], 0, 0, 0);
-    }
+    for (int g = 0; g < 4; ++g) dvdk_mfma(ql, gl, g);
   }
 
   if (kv_ok) {

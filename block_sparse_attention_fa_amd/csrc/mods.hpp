@@ -283,7 +283,9 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 // x2 for one key.  The forward's tile form gives y = x2 - m_ref directly,
 // folding the softmax reference max m_ref into the additive term, so the
 // exponential needs no separate subtraction: tile(row, kvb, m_ref), then
-// apply(tile, s, cr) for key kvb + cr.
+// apply(tile, s, cr) for key kvb + cr.  at(p, row(p, b, h, 0), q) equals
+// row(p, b, h, q) with only the per-query part recomputed (for kernels that
+// walk many query rows of one head).
 // ---------------------------------------------------------------------------
 
 struct ScoreNone {
@@ -293,6 +295,7 @@ struct ScoreNone {
     float c;
   };
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) { return {p.scale_log2}; }
+  static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int) { return r0; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) { return s * r.c; }
   struct Tile {
     float c, add;
@@ -316,6 +319,7 @@ struct ScoreAlibi {
     float slope = p.slopes ? p.slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)p.Hq);
     return {p.scale_log2, slope * kLog2e, q};
   }
+  static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int q) { return {r0.c, r0.sl, q}; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, r.sl * (float)(kv - r.q));
   }
@@ -344,6 +348,7 @@ struct ScoreSoftcap {
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) {
     return {p.tanh_k, p.cap_log2};
   }
+  static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int) { return r0; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) {
     float e = __builtin_amdgcn_exp2f(s * r.k);
     return fmaf(-2.0f * r.c2, __builtin_amdgcn_rcpf(1.0f + e), r.c2);
@@ -374,6 +379,7 @@ struct ScoreRelPos {
     int q;
   };
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int q) { return {p.scale_log2, q}; }
+  static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int q) { return {r0.c, q}; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, kLog2e * (float)(r.q - kv));
   }
@@ -399,6 +405,9 @@ struct ScoreBias {
   };
   static __device__ __forceinline__ Row row(const ScoreParams& p, int b, int h, int q) {
     return {p.scale_log2, p.bias + (long long)b * p.bs0 + (long long)h * p.bs1 + (long long)q * p.bs2};
+  }
+  static __device__ __forceinline__ Row at(const ScoreParams& p, const Row& r0, int q) {
+    return {r0.c, r0.row + (long long)q * p.bs2};
   }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(kLog2e, bf16_bits_to_float(r.row[kv]), s * r.c);
