@@ -303,6 +303,8 @@ void bwd_dkdv_kernel(BwdParams P) {
   // while sub-tile j + 1 loads
   __shared__ __align__(16) uint16_t q_lds[3][HB * D];
   __shared__ __align__(16) uint16_t g_lds[3][HB * D];
+  // base-2 LSE (first HB floats) and Delta (next HB) of the sub-tile's query rows
+  __shared__ __align__(16) float ld_lds[3][2 * HB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -407,6 +409,10 @@ void bwd_dkdv_kernel(BwdParams P) {
     const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1]);
     issue_one(Qh, qsb, q_lds[j % 3], q_voff, r0);
     issue_one(Gh, gsb, g_lds[j % 3], g_voff, r0);
+    if (wave == 0 && lane < 2 * HB / 4) {  // 16 bytes a lane; the workspace rows are padded
+      const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + r0 + 4 * (lane % (HB / 4));
+      dma16((lane < HB / 4 ? P.ws_lse2 : P.ws_delta) + w0, lds_address(ld_lds[j % 3]));
+    }
   };
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ rt_swizzle<D>(r)) * 8); };
   int aoff[KS];  // Q / dO rows as A operands: row lq (+32 per query block), chunk 2s + hh
@@ -456,8 +462,11 @@ void bwd_dkdv_kernel(BwdParams P) {
     }
   };
 
-  if (Jtot > 0) issue(0);
-  for (int j = 0; j < Jtot; ++j) {
+  // One sub-step; the ring stage j % 3 is a compile-time constant (the loop
+  // below is unrolled by 3) so that every LDS read address is a per-lane
+  // register plus an immediate offset.
+  auto step = [&](int j, auto stage) {
+    constexpr int st = decltype(stage)::value, sp = (st + 2) % 3;
     wait_vmcnt<0>();
     wait_lds_reads();
     __syncthreads();  // sub-step j landed; every wave is done with j - 2, whose stage j + 1 reuses
@@ -466,22 +475,14 @@ void bwd_dkdv_kernel(BwdParams P) {
     locate(j, hq, np, t, half);
     const int qs0 = col_entry(hq, np, t) * kBM + HB * half;  // first query row of the sub-step
     const bool partial = t < np;
-    const auto srow0 = Score::row(p.score, b, hq, 0);  // (before the MFMAs: it may branch)
+    const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);  // (may branch: before the MFMAs)
+    const int qlast = p.Sq - 1 - (qs0 + 4 * hh);
     const bool fix = partial | (qs0 + HB > p.Sq) | !kv_all;  // needs the zeroing pass below
-    const uint32_t qbase = lds_address(q_lds[j % 3]), gbase = lds_address(g_lds[j % 3]);
-    const uint32_t qprev = lds_address(q_lds[(j + 2) % 3]), gprev = lds_address(g_lds[(j + 2) % 3]);
-    // LSE and Delta of the 16 query rows of each block this lane holds: rows
-    // 8 (r / 4) + 4 hh + r % 4, four runs of four (padded rows exist); loaded
-    // here so they arrive while the MFMAs below run
-    const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + qs0 + 4 * hh;
-    f32x4_t lse4[2][4], del4[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lse4[mt][g] = *(const f32x4_t*)(P.ws_lse2 + w0 + 32 * mt + 8 * g);
-        del4[mt][g] = *(const f32x4_t*)(P.ws_delta + w0 + 32 * mt + 8 * g);
-      }
+    const uint32_t qbase = lds_address(q_lds[st]), gbase = lds_address(g_lds[st]);
+    const uint32_t qprev = lds_address(q_lds[sp]), gprev = lds_address(g_lds[sp]);
+    // LSE and Delta of this lane's rows 8 (r / 4) + 4 hh + r % 4 (+32 per query
+    // block): runs of four, read from LDS where the element-wise pass needs them
+    const uint32_t ldb = lds_address(ld_lds[st]) + 16 * hh;
 
     // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
@@ -499,14 +500,20 @@ void bwd_dkdv_kernel(BwdParams P) {
     // every 32 / (8 DT) elements.  Element (mt, r): query row
     // qs0 + 32 mt + 8 (r / 4) + 4 hh + r % 4 of this lane's key.
     constexpr int EPM = 32 / (8 * DT);  // elements per MFMA
+    f32x4_t l4, d4;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int mt = e >> 4, r = e & 15;
-      const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int dr = 32 * mt + 8 * (r >> 2) + (r & 3);  // query row qs0 + 4 hh + dr
+      if ((r & 3) == 0) {
+        l4 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldb + 4 * (32 * mt + 8 * (r >> 2)));
+        d4 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldb + 4 * (HB + 32 * mt + 8 * (r >> 2)));
+      }
       const float sv = sacc[mt][r];
-      const auto srow = Score::at(p.score, srow0, min(q, p.Sq - 1));
-      const float pv = __builtin_amdgcn_exp2f(Score::apply1(srow, sv, kvc, 0) - lse4[mt][r >> 2][r & 3]);
-      dpacc[mt][r] = pv * (dpacc[mt][r] - del4[mt][r >> 2][r & 3]) * Score::dmod1(srow, sv, kvc);
+      // functors that read memory get an in-bounds row past Sq (zeroed below)
+      const float pv = __builtin_amdgcn_exp2f(
+          Score::apply_col(scol, sv, Score::kReadsMemory ? min(dr, qlast) : dr) - l4[r & 3]);
+      dpacc[mt][r] = pv * (dpacc[mt][r] - d4[r & 3]) * Score::dmod_col(scol, sv);
       sacc[mt][r] = pv;
       if (e % EPM == EPM - 1) {
         const int i = e / EPM, ks = i / (2 * DT), dt = (i >> 1) % DT;
@@ -538,6 +545,12 @@ void bwd_dkdv_kernel(BwdParams P) {
         dsbo[g][k] = (__bf16)dpacc[mt][h8 + k];
       }
     }
+  };
+  if (Jtot > 0) issue(0);
+  for (int j = 0; j < Jtot; j += 3) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < Jtot) step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < Jtot) step(j + 2, std::integral_constant<int, 2>{});
   }
   if (Jtot > 0) {  // the last sub-step's dV / dK (its stage is still intact)
     const uint32_t ql = lds_address(q_lds[(Jtot - 1) % 3]), gl = lds_address(g_lds[(Jtot - 1) % 3]);

@@ -284,8 +284,11 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 // folding the softmax reference max m_ref into the additive term, so the
 // exponential needs no separate subtraction: tile(row, kvb, m_ref), then
 // apply(tile, s, cr) for key kvb + cr.  at(p, row(p, b, h, 0), q) equals
-// row(p, b, h, q) with only the per-query part recomputed (for kernels that
-// walk many query rows of one head).
+// row(p, b, h, q) with only the per-query part recomputed.  The column form
+// serves kernels where a lane holds one key kv and walks query rows q0 + dr:
+// col(p, row(p, b, h, 0), q0, kv) folds what is constant over the column,
+// apply_col(c, s, dr) gives x2 for query q0 + dr and dmod_col(c, s) the
+// derivative of the mod with respect to s (scaled scores, log2(e) excluded).
 // ---------------------------------------------------------------------------
 
 struct ScoreNone {
@@ -297,6 +300,10 @@ struct ScoreNone {
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int, int) { return {p.scale_log2}; }
   static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int) { return r0; }
   static __device__ __forceinline__ float apply1(const Row& r, float s, int, int) { return s * r.c; }
+  using Col = Row;
+  static __device__ __forceinline__ Col col(const ScoreParams&, const Row& r0, int, int) { return r0; }
+  static __device__ __forceinline__ float apply_col(const Col& c, float s, int) { return s * c.c; }
+  static __device__ __forceinline__ float dmod_col(const Col&, float) { return 1.0f; }
   struct Tile {
     float c, add;
   };
@@ -323,6 +330,16 @@ struct ScoreAlibi {
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, r.sl * (float)(kv - r.q));
   }
+  struct Col {
+    float c, nsl, add;  // add = sl * (kv - q0)
+  };
+  static __device__ __forceinline__ Col col(const ScoreParams&, const Row& r0, int q0, int kv) {
+    return {r0.c, -r0.sl, r0.sl * (float)(kv - q0)};
+  }
+  static __device__ __forceinline__ float apply_col(const Col& c, float s, int dr) {
+    return fmaf(s, c.c, fmaf(c.nsl, (float)dr, c.add));
+  }
+  static __device__ __forceinline__ float dmod_col(const Col&, float) { return 1.0f; }
   struct Tile {
     float c, sl, add;  // add = sl * (kvb - q) - m_ref
   };
@@ -353,6 +370,10 @@ struct ScoreSoftcap {
     float e = __builtin_amdgcn_exp2f(s * r.k);
     return fmaf(-2.0f * r.c2, __builtin_amdgcn_rcpf(1.0f + e), r.c2);
   }
+  using Col = Row;
+  static __device__ __forceinline__ Col col(const ScoreParams&, const Row& r0, int, int) { return r0; }
+  static __device__ __forceinline__ float apply_col(const Col& c, float s, int) { return apply1(c, s, 0, 0); }
+  static __device__ __forceinline__ float dmod_col(const Col& c, float s) { return dmod1(c, s, 0); }
   struct Tile {
     float k, neg2c2, add;  // add = cap*log2e - m_ref
   };
@@ -383,6 +404,16 @@ struct ScoreRelPos {
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(s, r.c, kLog2e * (float)(r.q - kv));
   }
+  struct Col {
+    float c, add;  // add = log2e * (q0 - kv)
+  };
+  static __device__ __forceinline__ Col col(const ScoreParams&, const Row& r0, int q0, int kv) {
+    return {r0.c, kLog2e * (float)(q0 - kv)};
+  }
+  static __device__ __forceinline__ float apply_col(const Col& c, float s, int dr) {
+    return fmaf(s, c.c, fmaf(kLog2e, (float)dr, c.add));
+  }
+  static __device__ __forceinline__ float dmod_col(const Col&, float) { return 1.0f; }
   struct Tile {
     float c, add;  // add = log2e * (q - kvb) - m_ref
   };
@@ -412,6 +443,18 @@ struct ScoreBias {
   static __device__ __forceinline__ float apply1(const Row& r, float s, int kv, int) {
     return fmaf(kLog2e, bf16_bits_to_float(r.row[kv]), s * r.c);
   }
+  struct Col {
+    float c;
+    const uint16_t* at;  // &bias[b, h, q0, kv]
+    long long rs;        // row stride (elements)
+  };
+  static __device__ __forceinline__ Col col(const ScoreParams& p, const Row& r0, int q0, int kv) {
+    return {r0.c, r0.row + (long long)q0 * p.bs2 + kv, p.bs2};
+  }
+  static __device__ __forceinline__ float apply_col(const Col& c, float s, int dr) {
+    return fmaf(kLog2e, bf16_bits_to_float(c.at[dr * c.rs]), s * c.c);
+  }
+  static __device__ __forceinline__ float dmod_col(const Col&, float) { return 1.0f; }
   struct Tile {
     float c, add;
     const uint16_t* row;  // bias[b, h, q, kvb:]
