@@ -50,31 +50,40 @@ __device__ __forceinline__ int rt_swizzle(int r) {
 }
 
 // ---- bwd_prep: Delta = rowsum(dO * O) and LSE * log2(e) per query row --------------
+// D / 8 lanes per row, 16 bytes of O and of dO each; 64 / (D / 8) rows per wave.
+template <int D>
+constexpr int kPrepRowsPerWave = 64 / (D / 8);
+
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams P) {
+  constexpr int LPR = D / 8;
   const FwdParams& p = P.f;
   const int lane = threadIdx.x & 63;
-  const long long gw = (long long)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);  // one wave per padded row
+  const long long gw = (long long)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  const long long gr = gw * kPrepRowsPerWave<D> + lane / LPR;  // padded row [b, h, q]
   const int Sp = P.sq_pad;
-  if (gw >= (long long)p.B * p.Hq * Sp) return;
-  const int q = (int)(gw % Sp);
-  const int bh = (int)(gw / Sp);
+  const bool live = gr < (long long)p.B * p.Hq * Sp;
+  const int q = (int)(gr % Sp);
+  const int bh = (int)(gr / Sp);
   const int b = bh / p.Hq, hq = bh % p.Hq;
-  float delta = 0.0f, lse2 = INFINITY;
-  if (q < p.Sq) {
-    const uint16_t* o = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)q * p.os[2];
-    const uint16_t* g = P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1] + (long long)q * P.dos[2];
-    float acc = 0.0f;
-    for (int d = lane; d < D; d += 64) acc = fmaf(bf16_bits_to_float(o[d]), bf16_bits_to_float(g[d]), acc);
+  float acc = 0.0f, lse2 = INFINITY;
+  if (live && q < p.Sq) {
+    const int d0 = 8 * (lane % LPR);
+    const u32x4_t o = *(const u32x4_t*)(p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)q * p.os[2] + d0);
+    const u32x4_t g = *(const u32x4_t*)(P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1] + (long long)q * P.dos[2] + d0);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    delta = acc;
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_bits_to_float(o[i] & 0xffffu), bf16_bits_to_float(g[i] & 0xffffu), acc);
+      acc = fmaf(bf16_bits_to_float(o[i] >> 16), bf16_bits_to_float(g[i] >> 16), acc);
+    }
     const float l = p.lse[((long long)b * p.Hq + hq) * p.Sq + q];
     lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
   }
-  if (lane == 0) {
-    P.ws_delta[gw] = delta;
-    P.ws_lse2[gw] = lse2;
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (live && lane % LPR == 0) {
+    P.ws_delta[gr] = acc;
+    P.ws_lse2[gr] = lse2;
   }
 }
 
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t k_voff = (uint32_t)(lrow * ksb + 16 * kchunk);
   const uint32_t v_voff = (uint32_t)(lrow * vsb + 16 * kchunk);
   auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int kv0) {
-    const uint32_t base = lds_address(buf) + 16 * 64 * wave;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf) + 16 * 64 * wave);
     if (kv0 + HB <= p.Skv) {
       const char* g0 = g + kv0 * rsb;
 #pragma unroll
@@ -201,9 +210,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int i = 0; i < DT; ++i) dq[i] = f32x16_t{};
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+  // One sub-tile; the ring stage j % 2 is a compile-time constant (the loop
+  // below is unrolled by 2) so that LDS reads take immediate offsets.
   const int J = SPT * T;
-  if (J > 0) issue(0);
-  for (int j = 0; j < J; ++j) {
+  auto step = [&](int j, auto stage) {
+    constexpr int stg = decltype(stage)::value;
     wait_vmcnt<0>();
     wait_lds_reads();
     __syncthreads();  // sub-tile j landed for every wave; every wave is done with j-1
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int kvt0 = kb_of(t) * kBN + HB * (j % SPT);
     const bool partial = t < n_part;
     const bool ragged = kvt0 + HB > p.Skv;
-    const uint32_t kbase = lds_address(k_lds[j % 2]), vbase = lds_address(v_lds[j % 2]);
+    const uint32_t kbase = lds_address(k_lds[stg]), vbase = lds_address(v_lds[stg]);
 
     // S^T = K Q^T and dP^T = V dO^T for this 64-key sub-tile
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
@@ -268,6 +279,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks], dq[dt], 0, 0, 0);
     }
+  };
+  if (J > 0) issue(0);
+  for (int j = 0; j < J; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < J) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   if (q_ok) {
@@ -387,7 +403,7 @@ void bwd_dkdv_kernel(BwdParams P) {
   const uint32_t q_voff = (uint32_t)(lrow * qsb + 16 * kchunk);
   const uint32_t g_voff = (uint32_t)(lrow * gsb + 16 * kchunk);
   auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int r0) {
-    const uint32_t base = lds_address(buf) + 16 * 64 * wave;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf) + 16 * 64 * wave);
     if (r0 + HB <= p.Sq) {
       const char* g0 = g + r0 * rsb;
 #pragma unroll
