@@ -49,6 +49,15 @@ __device__ __forceinline__ int rt_swizzle(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// A block-list entry at a wave-uniform address, read through the constant
+// address space so that it becomes a scalar load (the lists are written by an
+// earlier launch and do not change during this one).  A plain load here would
+// be a vector load, and the compiler's wait for it would also wait for the
+// LDS DMA in flight, which it cannot see.
+__device__ __forceinline__ int load_list(const int* p, long long i) {
+  return *(const __attribute__((address_space(4))) int*)(uintptr_t)(p + i);
+}
+
 // ---- bwd_prep: Delta = rowsum(dO * O) and LSE * log2(e) per query row --------------
 // D / 8 lanes per row, 16 bytes of O and of dO each; 64 / (D / 8) rows per wave.
 template <int D>
@@ -126,10 +135,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   } else {
     const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
     const long long row = ((long long)mb * bm.Hm + mh) * bm.NQ + qb;
-    n_part = bm.kv_num[row];
+    n_part = load_list(bm.kv_num, row);
     part_idx = bm.kv_idx + row * bm.NK;
     if (bm.separate_full) {
-      n_full = bm.full_num[row];
+      n_full = load_list(bm.full_num, row);
       full_idx = bm.full_idx + row * bm.NK;
     } else {
       n_full = 0;
@@ -137,8 +146,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
   const int T = n_part + n_full;
   auto kb_of = [&](int t) -> int {
-    if (t < n_part) return part_idx[t];
-    return bm.dense ? t - n_part : full_idx[t - n_part];
+    if (t < n_part) return load_list(part_idx, t);
+    return bm.dense ? t - n_part : load_list(full_idx, t - n_part);
   };
 
   const char* Kp = (const char*)(p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1]);
@@ -165,8 +174,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
   auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
-  auto issue = [&](int j) {
-    const int kv0 = kv0_of(j);
+  auto issue = [&](int kv0, int j) {
     issue_one(Kp, ksb, k_lds[j % 2], k_voff, kv0);
     issue_one(Vp, vsb, v_lds[j % 2], v_voff, kv0);
   };
@@ -213,14 +221,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // One sub-tile; the ring stage j % 2 is a compile-time constant (the loop
   // below is unrolled by 2) so that LDS reads take immediate offsets.
   const int J = SPT * T;
+  // first keys of sub-tiles j + 1 and j + 2: the list entry read in step j is
+  // in hand when step j + 1 issues its loads
+  int kv_nxt = 0, kv_nx2 = 0;
   auto step = [&](int j, auto stage) {
     constexpr int stg = decltype(stage)::value;
     wait_vmcnt<0>();
     wait_lds_reads();
     __syncthreads();  // sub-tile j landed for every wave; every wave is done with j-1
-    if (j + 1 < J) issue(j + 1);
+    const int kvt0 = kv_nxt;
+    kv_nxt = kv_nx2;
+    if (j + 1 < J) issue(kv_nxt, j + 1);
+    if (j + 2 < J) kv_nx2 = kv0_of(j + 2);
     const int t = j / SPT;
-    const int kvt0 = kb_of(t) * kBN + HB * (j % SPT);
     const bool partial = t < n_part;
     const bool ragged = kvt0 + HB > p.Skv;
     const uint32_t kbase = lds_address(k_lds[stg]), vbase = lds_address(v_lds[stg]);
@@ -280,7 +293,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks], dq[dt], 0, 0, 0);
     }
   };
-  if (J > 0) issue(0);
+  if (J > 0) {
+    kv_nxt = kv0_of(0);
+    issue(kv_nxt, 0);
+  }
+  if (J > 1) kv_nx2 = kv0_of(1);
   for (int j = 0; j < J; j += 2) {
     step(j, std::integral_constant<int, 0>{});
     if (j + 1 < J) step(j + 1, std::integral_constant<int, 1>{});
@@ -361,14 +378,14 @@ void bwd_dkdv_kernel(BwdParams P) {
     }
     const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
     const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
-    np = P.q_num[col];
-    nf = bm.separate_full ? P.full_q_num[col] : 0;
+    np = load_list(P.q_num, col);
+    nf = bm.separate_full ? load_list(P.full_q_num, col) : 0;
   };
   auto col_entry = [&](int hq, int np, int t) -> int {  // query tile of entry t
     if (bm.dense) return t;
     const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
     const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
-    return t < np ? P.q_idx[col * bm.NQ + t] : P.full_q_idx[col * bm.NQ + (t - np)];
+    return t < np ? load_list(P.q_idx, col * bm.NQ + t) : load_list(P.full_q_idx, col * bm.NQ + (t - np));
   };
   // sub-step j -> (query head, list entry, half); heads of the group in order.
   // The list lengths of the group's heads (at most 8) are read once.
@@ -417,16 +434,27 @@ void bwd_dkdv_kernel(BwdParams P) {
       }
     }
   };
-  auto issue = [&](int j) {
+  // sub-step j: its query head, first query row and whether its tile is partial
+  struct Sub {
+    int hq, qs0;
+    bool partial;
+  };
+  auto describe = [&](int j) -> Sub {
     int hq, np, t, half;
     locate(j, hq, np, t, half);
-    const int r0 = col_entry(hq, np, t) * kBM + HB * half;
-    const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1]);
-    const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)hq * P.dos[1]);
+    hq = __builtin_amdgcn_readfirstlane(hq);
+    np = __builtin_amdgcn_readfirstlane(np);
+    t = __builtin_amdgcn_readfirstlane(t);
+    return {hq, col_entry(hq, np, t) * kBM + HB * half, t < np};
+  };
+  auto issue = [&](const Sub& s, int j) {
+    const int r0 = s.qs0;
+    const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)s.hq * p.qs[1]);
+    const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)s.hq * P.dos[1]);
     issue_one(Qh, qsb, q_lds[j % 3], q_voff, r0);
     issue_one(Gh, gsb, g_lds[j % 3], g_voff, r0);
     if (wave == 0 && lane < 2 * HB / 4) {  // 16 bytes a lane; the workspace rows are padded
-      const long long w0 = ((long long)b * p.Hq + hq) * P.sq_pad + r0 + 4 * (lane % (HB / 4));
+      const long long w0 = ((long long)b * p.Hq + s.hq) * P.sq_pad + r0 + 4 * (lane % (HB / 4));
       dma16((lane < HB / 4 ? P.ws_lse2 : P.ws_delta) + w0, lds_address(ld_lds[j % 3]));
     }
   };
@@ -481,16 +509,20 @@ void bwd_dkdv_kernel(BwdParams P) {
   // One sub-step; the ring stage j % 3 is a compile-time constant (the loop
   // below is unrolled by 3) so that every LDS read address is a per-lane
   // register plus an immediate offset.
+  // Sub-step descriptors run two ahead: the list entry read for j + 2 in step j
+  // is in hand when step j + 1 issues its loads.
+  Sub nxt{0, 0, false}, nx2{0, 0, false};
   auto step = [&](int j, auto stage) {
     constexpr int st = decltype(stage)::value, sp = (st + 2) % 3;
     wait_vmcnt<0>();
     wait_lds_reads();
     __syncthreads();  // sub-step j landed; every wave is done with j - 2, whose stage j + 1 reuses
-    if (j + 1 < Jtot) issue(j + 1);
-    int hq, np, t, half;
-    locate(j, hq, np, t, half);
-    const int qs0 = col_entry(hq, np, t) * kBM + HB * half;  // first query row of the sub-step
-    const bool partial = t < np;
+    const Sub cur = nxt;
+    nxt = nx2;
+    if (j + 1 < Jtot) issue(nxt, j + 1);
+    if (j + 2 < Jtot) nx2 = describe(j + 2);
+    const int hq = cur.hq, qs0 = cur.qs0;  // query head, first query row of the sub-step
+    const bool partial = cur.partial;
     const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);  // (may branch: before the MFMAs)
     const int qlast = p.Sq - 1 - (qs0 + 4 * hh);
     const bool fix = partial | (qs0 + HB > p.Sq) | !kv_all;  // needs the zeroing pass below
@@ -502,13 +534,26 @@ void bwd_dkdv_kernel(BwdParams P) {
 
     // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
+    // A operands read PF pairs ahead of their MFMAs (one wave per SIMD: nothing
+    // else hides the LDS latency)
+    constexpr int PF = 3;
+    auto rd_q = [&](int i) { return *(const lds_bf16x8_t*)(uintptr_t)(qbase + 2 * (aoff[i % KS] + (i / KS) * 32 * D)); };
+    auto rd_g = [&](int i) { return *(const lds_bf16x8_t*)(uintptr_t)(gbase + 2 * (aoff[i % KS] + (i / KS) * 32 * D)); };
+    bf16x8_t aq[2 * KS], ag[2 * KS];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      aq[i] = rd_q(i);
+      ag[i] = rd_g(i);
+    }
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       const int mt = i / KS, s = i % KS;
-      const bf16x8_t aq = *(const lds_bf16x8_t*)(uintptr_t)(qbase + 2 * (aoff[s] + mt * 32 * D));
-      const bf16x8_t ag = *(const lds_bf16x8_t*)(uintptr_t)(gbase + 2 * (aoff[s] + mt * 32 * D));
-      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc[mt], 0, 0, 0);
-      dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vreg[s], dpacc[mt], 0, 0, 0);
+      if (i + PF < 2 * KS) {
+        aq[i + PF] = rd_q(i + PF);
+        ag[i + PF] = rd_g(i + PF);
+      }
+      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], kreg[s], sacc[mt], 0, 0, 0);
+      dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[i], vreg[s], dpacc[mt], 0, 0, 0);
     }
 
     // P and dS = P (dP - Delta) mod'(S) of sub-step j, in place of S and dP,
@@ -562,7 +607,11 @@ void bwd_dkdv_kernel(BwdParams P) {
       }
     }
   };
-  if (Jtot > 0) issue(0);
+  if (Jtot > 0) {
+    nxt = describe(0);
+    issue(nxt, 0);
+  }
+  if (Jtot > 1) nx2 = describe(1);
   for (int j = 0; j < Jtot; j += 3) {
     step(j, std::integral_constant<int, 0>{});
     if (j + 1 < Jtot) step(j + 1, std::integral_constant<int, 1>{});

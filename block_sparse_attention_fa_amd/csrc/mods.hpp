@@ -31,6 +31,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// A read-only parameter at a wave-uniform address, read through the constant
+// address space (a scalar load).
+__device__ __forceinline__ float load_param(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)(uintptr_t)p;
+}
+
 // ---------------------------------------------------------------------------
 // mask_mods
 //
@@ -323,7 +329,7 @@ struct ScoreAlibi {
     int q;
   };
   static __device__ __forceinline__ Row row(const ScoreParams& p, int, int h, int q) {
-    float slope = p.slopes ? p.slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)p.Hq);
+    float slope = p.slopes ? load_param(p.slopes + h) : exp2f(-8.0f * (float)(h + 1) / (float)p.Hq);
     return {p.scale_log2, slope * kLog2e, q};
   }
   static __device__ __forceinline__ Row at(const ScoreParams&, const Row& r0, int q) { return {r0.c, r0.sl, q}; }
