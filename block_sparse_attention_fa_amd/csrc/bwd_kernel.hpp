@@ -255,30 +255,33 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const float m_ref = lse2;
     const auto st = Score::tile(srow, kvb, m_ref);
     const auto mtl = Mask::tile(mrow, kvb);
+    // computed for every element first (no branches), then the mask and the
+    // ragged tail zeroed on the tiles that have them
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int mt = e >> 4, r = e & 15;
+      const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+      const int crs = Score::kReadsMemory ? min(cr, lim - 1) : cr;  // in-bounds key for functors that read memory
+      const float sv = sacc[mt][r];
+      const float pv = __builtin_amdgcn_exp2f(Score::apply(st, sv, crs));
+      dpacc[mt][r] = pv * (dpacc[mt][r] - delta) * Score::dmod1(srow, sv, kvb + crs);
+    }
+    if (partial || ragged) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int mt = e >> 4, r = e & 15;
+        const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+        bool keep = cr < lim;
+        if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+        dpacc[mt][r] = keep ? dpacc[mt][r] : 0.0f;
+      }
+    }
     bf16x8_t dsb[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int mt = g >> 1, h8 = 8 * (g & 1);
-      bf16x2_t pk[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float dsv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = h8 + 2 * k + u;
-          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-          const int crs = min(cr, lim - 1);  // in-bounds key for functors that read memory
-          const float sv = sacc[mt][r];
-          bool keep = cr < lim;
-          if (partial) keep = keep && Mask::keep(mtl, crs);
-          const float pv = keep ? __builtin_amdgcn_exp2f(Score::apply(st, sv, Score::kReadsMemory ? crs : cr)) : 0.0f;
-          dsv[u] = pv * (dpacc[mt][r] - delta) * Score::dmod1(srow, sv, kvb + crs);
-        }
-        pk[k][0] = (__bf16)dsv[0];
-        pk[k][1] = (__bf16)dsv[1];
-      }
-      dsb[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
-                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int k = 0; k < 8; ++k) dsb[g][k] = (__bf16)dpacc[mt][h8 + k];
     }
 
     // dQ^T += K^T dS^T
