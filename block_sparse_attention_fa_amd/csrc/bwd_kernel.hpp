@@ -384,36 +384,35 @@ void bwd_dkdv_kernel(BwdParams P) {
     np = load_list(P.q_num, col);
     nf = bm.separate_full ? load_list(P.full_q_num, col) : 0;
   };
-  auto col_entry = [&](int hq, int np, int t) -> int {  // query tile of entry t
-    if (bm.dense) return t;
-    const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hq : 0;
-    const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
-    return t < np ? load_list(P.q_idx, col * bm.NQ + t) : load_list(P.full_q_idx, col * bm.NQ + (t - np));
-  };
-  // sub-step j -> (query head, list entry, half); heads of the group in order.
-  // The list lengths of the group's heads (at most 8) are read once.
-  int cnt_p[8], cnt_n[8];
+  // Sub-steps: the group's heads in order, each head's column list (partial
+  // entries, then full ones), SPT sub-steps per entry.
   int Jtot = 0;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    int np = 0, nf = 0;
-    if (g < p.G) col_counts(hkv * p.G + g, np, nf);
-    cnt_p[g] = np;
-    cnt_n[g] = SPT * (np + nf);
-    Jtot += cnt_n[g];
+  for (int g = 0; g < p.G; ++g) {
+    int np, nf;
+    col_counts(hkv * p.G + g, np, nf);
+    Jtot += SPT * (np + nf);
   }
-  auto locate = [&](int j, int& hq, int& np, int& t, int& half) {
-    int g = 0;
-#pragma unroll
-    for (int i = 0; i < 7; ++i)
-      if (g == i && j >= cnt_n[i]) {
-        j -= cnt_n[i];
-        g = i + 1;
-      }
-    hq = hkv * p.G + g;
-    np = cnt_p[g];
-    t = j / SPT;
-    half = j % SPT;
+  // A cursor walks them in order (sub-steps are described one after another):
+  // head cg with cnp partial and cnt entries in all, entry ct, half ch, and
+  // the head's two lists.
+  int cg = -1, cnp = 0, cnt = 0, ct = 0, ch = 0;
+  const int* plist = nullptr;
+  const int* flist = nullptr;
+  auto next_head = [&]() {  // the next head with a non-empty list (the caller knows one exists)
+    do {
+      ++cg;
+      int nf;
+      col_counts(hkv * p.G + cg, cnp, nf);
+      cnt = cnp + nf;
+    } while (cnt == 0);
+    if (!bm.dense) {
+      const int mb = bm.Bm > 1 ? b : 0, mh = bm.Hm > 1 ? hkv * p.G + cg : 0;
+      const long long col = ((long long)mb * bm.Hm + mh) * bm.NK + kb;
+      plist = P.q_idx + col * bm.NQ;
+      flist = P.full_q_idx + col * bm.NQ;
+    }
+    ct = 0;
+    ch = 0;
   };
 
   constexpr int RPI = 64 / CPR;
@@ -442,13 +441,16 @@ void bwd_dkdv_kernel(BwdParams P) {
     int hq, qs0;
     bool partial;
   };
-  auto describe = [&](int j) -> Sub {
-    int hq, np, t, half;
-    locate(j, hq, np, t, half);
-    hq = __builtin_amdgcn_readfirstlane(hq);
-    np = __builtin_amdgcn_readfirstlane(np);
-    t = __builtin_amdgcn_readfirstlane(t);
-    return {hq, col_entry(hq, np, t) * kBM + HB * half, t < np};
+  auto describe = [&]() -> Sub {  // the sub-step after the last one described
+    if (ch == SPT) {
+      ch = 0;
+      ++ct;
+    }
+    if (cg < 0 || ct == cnt) next_head();
+    const int qt = bm.dense ? ct : (ct < cnp ? load_list(plist, ct) : load_list(flist, ct - cnp));
+    const Sub s{hkv * p.G + cg, qt * kBM + HB * ch, ct < cnp};
+    ++ch;
+    return s;
   };
   auto issue = [&](const Sub& s, int j) {
     const int r0 = s.qs0;
@@ -523,7 +525,7 @@ void bwd_dkdv_kernel(BwdParams P) {
     const Sub cur = nxt;
     nxt = nx2;
     if (j + 1 < Jtot) issue(nxt, j + 1);
-    if (j + 2 < Jtot) nx2 = describe(j + 2);
+    if (j + 2 < Jtot) nx2 = describe();
     const int hq = cur.hq, qs0 = cur.qs0;  // query head, first query row of the sub-step
     const bool partial = cur.partial;
     const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);  // (may branch: before the MFMAs)
@@ -611,10 +613,10 @@ void bwd_dkdv_kernel(BwdParams P) {
     }
   };
   if (Jtot > 0) {
-    nxt = describe(0);
+    nxt = describe();
     issue(nxt, 0);
   }
-  if (Jtot > 1) nx2 = describe(1);
+  if (Jtot > 1) nx2 = describe();
   for (int j = 0; j < Jtot; j += 3) {
     step(j, std::integral_constant<int, 0>{});
     if (j + 1 < Jtot) step(j + 1, std::integral_constant<int, 1>{});
