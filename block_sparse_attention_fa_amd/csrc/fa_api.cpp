@@ -94,6 +94,7 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
   if ((st = check_strides("v", a->v_stride, a->v)) != FA_OK) return st;
   if ((st = check_strides("o", a->o_stride, a->o)) != FA_OK) return st;
   if (!(isfinite(a->scale)) || a->scale < 0.0f) return fail(FA_ERR_SHAPE, "scale must be finite and >= 0");
+  if (a->scale > 0.0f && a->scale < 1e-20f) return fail(FA_ERR_SHAPE, "scale must be 0 (default) or >= 1e-20");
 
   const int NQ = ceil_div(a->Sq, FA_BLOCK), NK = ceil_div(a->Skv, FA_BLOCK);
   if ((long long)NQ * a->Hq * a->B > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many query tiles");

@@ -291,6 +291,13 @@ void fwd_kernel(FwdParams p) {
   }
   const auto mrow = Mask::row(p.mask, b, hq, qc);
   const auto srow = Score::row(p.score, b, hq, qc);
+  // Starting value of every QK^T accumulation: zero, or the score's key-offset
+  // term (the same for every lane and both 32-key blocks).
+  f32x16_t acc0 = f32x16_t{};
+  if constexpr (Score::kPreload) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc0[r] = Score::preload(srow, 8 * (r >> 2) + (r & 3));
+  }
 
   // ---- online softmax state (base-2 units) ----------------------------------
   f32x16_t oacc[DT];
@@ -336,7 +343,7 @@ void fwd_kernel(FwdParams p) {
   auto qk_mfma = [&](f32x16_t (&acc)[2], int i) {
     const int mt = i / KS, s = i % KS;
     const bf16x8_t a = ((const lds_bf16x8_t*)(uintptr_t)kaddr[s])[mt * 32 * D / 8];
-    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], acc[mt], 0, 0, 0);
+    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? acc0 : acc[mt], 0, 0, 0);
   };
   // MFMA i (0..4*DT-1) of O^T += V^T P^T: (16-key k-step i / DT of the sub-tile, d block i % DT).
   // V^T comes from row-major V through ds_read_b64_tr_b16.
@@ -372,8 +379,7 @@ void fwd_kernel(FwdParams p) {
       wait_vmcnt<NI>();
     wait_lds_reads();
     __syncthreads();
-    f32x16_t s_a[2] = {f32x16_t{}, f32x16_t{}};
-    f32x16_t s_b[2];
+    f32x16_t s_a[2], s_b[2];  // (each accumulation starts from acc0)
     set_k_stage(k_lds[0]);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) qk_mfma(s_a, i);
@@ -435,6 +441,8 @@ void fwd_kernel(FwdParams p) {
         if constexpr (BL) {  // element (mt, r) is component r % 4 of chunk 4 mt + r / 4
           const uint32_t w = bias2[4 * mt + (r >> 2)][(r >> 1) & 1];
           y = Score::apply_bits(st, s_cur[mt][r], (r & 1) ? (w >> 16) : (w & 0xffffu));
+        } else if constexpr (Score::kPreload) {  // the key-offset term within the block is in the accumulator
+          y = Score::apply_pre(st, s_cur[mt][r], mt);
         } else {
           // functors that read memory get an in-bounds key on the ragged tile
           y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
@@ -496,8 +504,6 @@ void fwd_kernel(FwdParams p) {
       }
 
       // ---- D: P of j  ||  S of j+1
-      s_nxt[0] = f32x16_t{};
-      s_nxt[1] = f32x16_t{};
 #pragma unroll
       for (int g = 0; g < 4; ++g) {  // 16-key k-step g of the PV product
         const int mt = g >> 1, h8 = 8 * (g & 1);

@@ -295,10 +295,16 @@ __host__ __device__ inline bool dispatch_mask(int kind, F&& f) {
 // col(p, row(p, b, h, 0), q0, kv) folds what is constant over the column,
 // apply_col(c, s, dr) gives x2 for query q0 + dr and dmod_col(c, s) the
 // derivative of the mod with respect to s (scaled scores, log2(e) excluded).
+//
+// Functors whose score is linear in s plus a term linear in the key offset set
+// kPreload: the forward then starts each QK^T accumulation from preload(row, c)
+// (c = key offset inside a 32-key block, 0..31) and applies apply_pre(tile, acc,
+// mt) = apply(tile, s, 32 mt + c), one multiply-add per element.
 // ---------------------------------------------------------------------------
 
 struct ScoreNone {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
   struct Row {
     float c;
@@ -322,6 +328,7 @@ struct ScoreNone {
 // Concepts "score_mod": s + slope[h] * (kv - q).
 struct ScoreAlibi {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kPreload = true;
   static constexpr bool kStagesBias = false;
   struct Row {
     float c;    // scale * log2e
@@ -355,6 +362,11 @@ struct ScoreAlibi {
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(t.sl, (float)cr, t.add));
   }
+  // s + sl c / (scale log2e): the key-offset term in units of the raw dot product
+  static __device__ __forceinline__ float preload(const Row& r, int c) { return r.sl * (float)c / r.c; }
+  static __device__ __forceinline__ float apply_pre(const Tile& t, float acc, int mt) {
+    return fmaf(acc, t.c, fmaf(t.sl, (float)(32 * mt), t.add));
+  }
   static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
@@ -363,6 +375,7 @@ struct ScoreAlibi {
 // reciprocal; the error this adds is measured against fp64 tanh in the tests.
 struct ScoreSoftcap {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
   struct Row {
     float k;     // 2 * scale / cap * log2e
@@ -400,6 +413,7 @@ struct ScoreSoftcap {
 // Talk summary (score mode) / Concepts "Debugging score_mods": s + (q - kv).
 struct ScoreRelPos {
   static constexpr bool kReadsMemory = false;
+  static constexpr bool kPreload = true;
   static constexpr bool kStagesBias = false;
   struct Row {
     float c;
@@ -429,12 +443,17 @@ struct ScoreRelPos {
   static __device__ __forceinline__ float apply(const Tile& t, float s, int cr) {
     return fmaf(s, t.c, fmaf(-kLog2e, (float)cr, t.add));
   }
+  static __device__ __forceinline__ float preload(const Row& r, int c) { return -kLog2e * (float)c / r.c; }
+  static __device__ __forceinline__ float apply_pre(const Tile& t, float acc, int mt) {
+    return fmaf(acc, t.c, fmaf(-kLog2e, (float)(32 * mt), t.add));
+  }
   static __device__ __forceinline__ float dmod1(const Row&, float, int) { return 1.0f; }
 };
 
 // Dynamic-bias feature request (attention-gym issue 123): s + bias[b,h,q,kv].
 struct ScoreBias {
   static constexpr bool kReadsMemory = true;
+  static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
   struct Row {
     float c;

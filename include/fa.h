@@ -149,7 +149,7 @@ typedef struct {
   float* lse;                 /* optional fp32 [B,Hq,Sq] contiguous, natural-log LSE; -inf for empty rows */
   int64_t q_stride[4], k_stride[4], v_stride[4], o_stride[4];
   int32_t B, Hq, Hkv, Sq, Skv, D; /* D in {64, 128} */
-  float scale;                /* 0 => 1/sqrt(D) */
+  float scale;                /* 0 => 1/sqrt(D); otherwise >= 1e-20 */
   const fa_block_mask* block_mask; /* NULL => dense attention without a mask */
   fa_score_desc score;
   int32_t num_splits;         /* decode: max KV splits per sequence, 0 = auto; ignored by fa_forward */
