@@ -87,6 +87,11 @@ def test_forward_validation_codes():
     a = _args(); a.B = 0
     assert _status(a) == fa.FA_ERR_SHAPE
     assert "sizes must be positive" in fa.lib().fa_last_error().decode()
+    a = _args(); a.scale = -1.0
+    assert _status(a) == fa.FA_ERR_SHAPE
+    a = _args(); a.scale = 1e-30  # too small for the preloaded key-offset term
+    assert _status(a) == fa.FA_ERR_SHAPE
+    assert "scale" in fa.lib().fa_last_error().decode()
 
 
 def _bm(Bm=1, Hm=1, NQ=2, NK=2, kind=fa.MASK_CAUSAL, Sq=256, Skv=256):
