@@ -537,6 +537,16 @@ void bwd_dkdv_kernel(BwdParams P) {
     // block): runs of four, read from LDS where the element-wise pass needs them
     const uint32_t ldb = lds_address(ld_lds[st]) + 16 * hh;
 
+    // Transposed operands of the delayed dV / dK MFMAs (sub-step j - 1, whose
+    // stage is already in LDS): MFMA i reads k-step i / (2 DT), d block
+    // (i / 2) % DT, dO^T for even i (dV) and Q^T for odd i (dK).  The first
+    // PFT are read now; each later one PFT MFMAs before its use.
+    constexpr int NM = 8 * DT, PFT = 4;
+    auto tr_op = [&](int i) { return tr_read((i & 1) ? qprev : gprev, (i >> 1) % DT, i / (2 * DT)); };
+    bf16x8_t tro[NM];
+#pragma unroll
+    for (int i = 0; i < PFT; ++i) tro[i] = tr_op(i);
+
     // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
     // A operands read PF pairs ahead of their MFMAs (one wave per SIMD: nothing
@@ -583,10 +593,11 @@ void bwd_dkdv_kernel(BwdParams P) {
       sacc[mt][r] = pv;
       if (e % EPM == EPM - 1) {
         const int i = e / EPM, ks = i / (2 * DT), dt = (i >> 1) % DT;
+        if (i + PFT < NM) tro[i + PFT] = tr_op(i + PFT);
         if (i & 1)
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qprev, dt, ks), dsbo[ks], dk[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], dsbo[ks], dk[dt], 0, 0, 0);
         else
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gprev, dt, ks), pbo[ks], dv[dt], 0, 0, 0);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], pbo[ks], dv[dt], 0, 0, 0);
       }
     }
     // Zero what the mask drops (partial tiles), rows past Sq and a key past Skv
