@@ -63,3 +63,38 @@ def test_backward_superset_dense_per_head_and_scale():
     run_bwd(54, "none", "alibi", 1, 4, 1, 200, 200, 64, dense=True)
     run_bwd(55, "sliding_causal", "none", 1, 4, 4, 300, 300, 128, per_head=True)
     run_bwd(56, "causal", "rel_pos", 2, 8, 1, 160, 160, 128, scale=0.05)
+
+
+@pytest.mark.parametrize("empty_heads", [(1, 3), (0, 2)])
+def test_backward_gqa_heads_with_empty_lists(empty_heads):
+    """A per-head BlockMask whose lists are emptied for some query heads of a
+    GQA group: those heads attend nothing (O = 0, LSE = -inf, zero gradients),
+    and the dK/dV kernel, which walks the group's heads in order, must skip
+    them wherever they sit (first, middle or last)."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    seed, B, Hq, Hkv, S, D = 57, 1, 4, 1, 300, 128
+    print(f"[case] bwd GQA empty heads {empty_heads} B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}", flush=True)
+    q, k, v = gen.qkv(seed, B, Hq, Hkv, S, S, D)
+    dO = gen._normal_bf16([seed, 30], (B, Hq, S, D), 1.0)
+    qt, kt, vt, dOt = (gen.to_torch_bf16(x) for x in (q, k, v, dO))
+    bm = fa.fa_build_block_mask(fa.MaskMod("causal"), 1, Hq, S, S, transposed=True)
+    for h in empty_heads:
+        for t in (bm.kv_num_blocks, bm.full_kv_num_blocks, bm.q_num_blocks, bm.full_q_num_blocks):
+            t[:, h].zero_()
+    sc = fa.ScoreMod("alibi")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=sc, lse=lse)
+    dq, dk, dv = fa.fa_backward(qt, kt, vt, out, lse, dOt, block_mask=bm, score=sc)
+    torch.cuda.synchronize()
+    empty = np.array(empty_heads)
+    mask = lambda b, h, qq, kv: (qq >= kv) & ~np.isin(h, empty)
+    score = fo.alibi(fo.default_alibi_slopes(Hq))
+    O_ref, L_ref = fo.attention(q, k, v, mask, score)
+    got_o = gen.bf16_bits_to_f32(gen.from_torch_bf16(out)).astype(np.float64)
+    assert np.all(got_o[:, list(empty_heads)] == 0.0)
+    assert np.all(np.isneginf(lse[:, list(empty_heads)].cpu().numpy()))
+    assert np.abs(got_o - O_ref).max() <= C.TOL_MAX
+    refs = fo.attention_backward(q, k, v, dO, mask, score)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        compare_grad(gen.bf16_bits_to_f32(gen.from_torch_bf16(g)), r, f"{name} GQA empty heads {empty_heads}")
