@@ -560,8 +560,7 @@ void bwd_dkdv_kernel(BwdParams P) {
       aq[i] = rd_q(i);
       ag[i] = rd_g(i);
     }
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
+    auto sdp_mfma = [&](int i) {  // k-step i % KS of query block i / KS
       const int mt = i / KS, s = i % KS;
       if (i + PF < 2 * KS) {
         aq[i + PF] = rd_q(i + PF);
@@ -569,13 +568,18 @@ void bwd_dkdv_kernel(BwdParams P) {
       }
       sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], kreg[s], sacc[mt], 0, 0, 0);
       dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[i], vreg[s], dpacc[mt], 0, 0, 0);
-    }
+    };
+    // query block 0 now; block 1 beside the element-wise work of block 0 below
+#pragma unroll
+    for (int i = 0; i < KS; ++i) sdp_mfma(i);
 
     // P and dS = P (dP - Delta) mod'(S) of sub-step j, in place of S and dP,
     // with one MFMA of dV^T += dO^T P or dK^T += Q^T dS of sub-step j - 1 after
-    // every 32 / (8 DT) elements.  Element (mt, r): query row
+    // every 32 / (8 DT) elements, and during query block 0 the S and dP
+    // products of block 1.  Element (mt, r): query row
     // qs0 + 32 mt + 8 (r / 4) + 4 hh + r % 4 of this lane's key.
-    constexpr int EPM = 32 / (8 * DT);  // elements per MFMA
+    constexpr int EPM = 32 / (8 * DT);  // elements per dV / dK MFMA
+    constexpr int EPS = 16 / KS;        // elements per S / dP pair of block 1
     f32x4_t l4, d4;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
@@ -599,6 +603,7 @@ void bwd_dkdv_kernel(BwdParams P) {
         else
           dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], pbo[ks], dv[dt], 0, 0, 0);
       }
+      if (mt == 0 && e % EPS == EPS - 1) sdp_mfma(KS + e / EPS);
     }
     // Zero what the mask drops (partial tiles), rows past Sq and a key past Skv
     if (fix) {
