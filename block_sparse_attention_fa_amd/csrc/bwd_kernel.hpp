@@ -238,55 +238,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const bool ragged = kvt0 + HB > p.Skv;
     const uint32_t kbase = lds_address(k_lds[stg]), vbase = lds_address(v_lds[stg]);
 
-    // S^T = K Q^T and dP^T = V dO^T for this 64-key sub-tile
+    // S^T = K Q^T and dP^T = V dO^T for this 64-key sub-tile: key block 0
+    // first; block 1 beside the element-wise work of block 0, and dQ's first
+    // two k-steps (which need only block 0's dS) beside that of block 1
     f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
+    auto sdp_mfma = [&](int i) {
       const int mt = i / KS, s = i % KS;
       const bf16x8_t ak = *(const lds_bf16x8_t*)(uintptr_t)(kbase + 2 * (koff[s] + mt * 32 * D));
       const bf16x8_t av = *(const lds_bf16x8_t*)(uintptr_t)(vbase + 2 * (koff[s] + mt * 32 * D));
       sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc[mt], 0, 0, 0);
       dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], dpacc[mt], 0, 0, 0);
-    }
-
-    // dS^T = P (dP - Delta) mod'(S); element (mt, r) is key kvb + cr
-    const int kvb = kvt0 + 4 * hh;
-    const int lim = ragged ? p.Skv - kvb : HB;
-    const float m_ref = lse2;
-    const auto st = Score::tile(srow, kvb, m_ref);
-    const auto mtl = Mask::tile(mrow, kvb);
-    // computed for every element first (no branches), then the mask and the
-    // ragged tail zeroed on the tiles that have them
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int mt = e >> 4, r = e & 15;
-      const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-      const int crs = Score::kReadsMemory ? min(cr, lim - 1) : cr;  // in-bounds key for functors that read memory
-      const float sv = sacc[mt][r];
-      const float pv = __builtin_amdgcn_exp2f(Score::apply(st, sv, crs));
-      dpacc[mt][r] = pv * (dpacc[mt][r] - delta) * Score::dmod1(srow, sv, kvb + crs);
-    }
-    if (partial || ragged) {
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int mt = e >> 4, r = e & 15;
-        const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-        bool keep = cr < lim;
-        if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
-        dpacc[mt][r] = keep ? dpacc[mt][r] : 0.0f;
-      }
-    }
+    };
     bf16x8_t dsb[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int mt = g >> 1, h8 = 8 * (g & 1);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dsb[g][k] = (__bf16)dpacc[mt][h8 + k];
-    }
-
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
+    auto dq_mfma = [&](int i) {  // dQ^T += K^T dS^T, k-step i / DT, d block i % DT
       const int ks = i / DT, dt = i % DT;
       const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4_t*)(uintptr_t)(kbase + 2 * (ktlo[dt] + ks * 16 * D)));
@@ -294,7 +258,46 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
           (lds_bf16x4_t*)(uintptr_t)(kbase + 2 * (kthi[dt] + ks * 16 * D)));
       const bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[ks], dq[dt], 0, 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < KS; ++i) sdp_mfma(i);
+
+    // dS^T = P (dP - Delta) mod'(S); element (mt, r) is key kvb + cr.  Each
+    // block is computed for every element first (no branches), then the mask
+    // and the ragged tail are zeroed on the tiles that have them.
+    const int kvb = kvt0 + 4 * hh;
+    const int lim = ragged ? p.Skv - kvb : HB;
+    const float m_ref = lse2;
+    const auto st = Score::tile(srow, kvb, m_ref);
+    const auto mtl = Mask::tile(mrow, kvb);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+        const int crs = Score::kReadsMemory ? min(cr, lim - 1) : cr;  // in-bounds key for functors that read memory
+        const float sv = sacc[mt][r];
+        const float pv = __builtin_amdgcn_exp2f(Score::apply(st, sv, crs));
+        dpacc[mt][r] = pv * (dpacc[mt][r] - delta) * Score::dmod1(srow, sv, kvb + crs);
+        if (mt == 0 && r % (16 / KS) == 16 / KS - 1) sdp_mfma(KS + r / (16 / KS));
+        if (mt == 1 && r % (8 / DT) == 8 / DT - 1) dq_mfma(r / (8 / DT));
+      }
+      if (partial || ragged) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+          bool keep = cr < lim;
+          if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+          dpacc[mt][r] = keep ? dpacc[mt][r] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int g = 2 * mt; g < 2 * mt + 2; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dsb[g][k] = (__bf16)dpacc[mt][8 * (g & 1) + k];
     }
+#pragma unroll
+    for (int i = 2 * DT; i < 4 * DT; ++i) dq_mfma(i);
   };
   if (J > 0) {
     kv_nxt = kv0_of(0);
