@@ -291,7 +291,8 @@ def main():
             fa.fa_backward(qt, kt, vt, out, lse, dot, block_mask=bmt, score=score, dq=dq, dk=dk, dv=dv,
                            workspace=wsb)
 
-        bwd_settle, bwd_steps = 5, 10  # ~10 ms per call: 5 calls settle the clock
+        # ~4 ms per call; the clock keeps rising over the first 15-20 calls
+        bwd_settle, bwd_steps = 30, 10
         for _ in range(bwd_settle):
             bwd()
         torch.cuda.synchronize()
