@@ -8,7 +8,7 @@ split-KV decode (B=32, Hq=32, Hkv=8, D=128, KV cache 32768 with valid lengths
 uniform in [4096, 32768], softcap 50) is timed in the same run and reported as
 HBM GB/s.  Inputs are resident in HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 30]   (at least 30 untimed steps)
+    python bench.py [--gpus 1] [--steps 20] [--warmup 100]   (at least 30 untimed steps)
     python bench.py --ablation                              (block-skipping ablation, sparsity sweep)
 """
 
@@ -160,7 +160,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
