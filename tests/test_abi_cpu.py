@@ -239,3 +239,39 @@ def test_backward_lds_swizzle_is_conflict_free(D):
     step = 16 if D == 128 else 32  # rows between the DMA loads of one lane
     for lrow in range(64):
         assert len({_rt_swizzle(D, lrow + step * i) for i in range(4)}) == 1
+
+
+def test_backward_validation_codes():
+    """fa_backward rejects bad arguments on the host, before any launch."""
+    L = fa.lib()
+
+    def grads(ptr=0x10000):
+        g = fa.GradArgs()
+        g.dout = g.dq = g.dk = g.dv = ptr
+        for name in ("dout_stride", "dq_stride", "dk_stride", "dv_stride"):
+            st = getattr(g, name)
+            st[0], st[1], st[2], st[3] = 2 * 256 * 64, 256 * 64, 64, 1
+        return g
+
+    def bwd(a, g, ws=0x20000, nbytes=1 << 30):
+        return L.fa_backward(ctypes.byref(a), None if g is None else ctypes.byref(g), ws, nbytes, None)
+
+    a = _args(); a.lse = 0x30000
+    n = ctypes.c_size_t()
+    assert L.fa_backward_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    assert n.value == 2 * 4 * 1 * 2 * 256            # LSE and Delta, fp32, rows padded to 128
+    assert bwd(a, None) == fa.FA_ERR_NULL
+    a2 = _args()                                         # no LSE
+    assert bwd(a2, grads()) == fa.FA_ERR_NULL
+    assert "LSE" in L.fa_last_error().decode()
+    g = grads(); g.dq = 0
+    assert bwd(a, g) == fa.FA_ERR_NULL
+    g = grads(); g.dk = 0x10008                          # not 16-byte aligned
+    assert bwd(a, g) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(a, grads(), ws=0) == fa.FA_ERR_WORKSPACE
+    assert bwd(a, grads(), nbytes=n.value - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd(a, grads(), ws=0x20008) == fa.FA_ERR_WORKSPACE
+    bm = _bm()                                           # BlockMask without its transposed view
+    a.block_mask = ctypes.pointer(bm)
+    assert bwd(a, grads()) == fa.FA_ERR_NULL
+    assert "transposed view" in L.fa_last_error().decode()
