@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int SPT = kBN / HB;
   constexpr int NI = HB * CPR / 64 / 4;
   const FwdParams& p = P.f;
-  // K and V sub-tiles, both row-major with the K chunk swizzle, 2-deep ring
+  // K and V sub-tiles, row-major with the row/transposed swizzle, 2-deep ring
   __shared__ __align__(16) uint16_t k_lds[2][HB * D];
   __shared__ __align__(16) uint16_t v_lds[2][HB * D];
 
