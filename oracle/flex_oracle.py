@@ -81,7 +81,10 @@ def causal():
 
 
 def sliding_window(window: int):
-    """The window term of Concepts "Composing masks": q - kv <= window (inclusive)."""
+    """The window term of Concepts "Composing masks": q - kv <= window (inclusive).
+
+    On its own it only bounds how far back a key may lie, so every later key
+    (kv > q) is kept; the page ANDs it with causal to get the sliding band."""
     return lambda b, h, q, kv: (q - kv) <= window
 
 
@@ -491,7 +494,10 @@ def sparsity(cls: np.ndarray) -> float:
 
 
 def attended_count(mask_mod, B: int, H: int, Sq: int, Skv: int, chunk: int = 1024) -> int:
-    """Number of (b, h, q, kv) positions the mask keeps (work actually attended)."""
+    """Number of (b, h, q, kv) positions the mask keeps: the attended work that
+    attended FLOPs (4 D per position) are counted on.  mask_mod None keeps all."""
+    if mask_mod is None:
+        return B * H * Sq * Skv
     n = 0
     kv_all = np.arange(Skv, dtype=np.int64)[None, :]
     for b in range(B):

@@ -38,6 +38,12 @@ MUTANTS = [
      [pins.test_equal_scores_lse_is_log_count]),
     ("window_exclusive", "(q - kv) <= window", "(q - kv) < window",
      [pins.test_sliding_window_zero_is_identity_on_v, pins.test_mask_limits]),
+    ("window_two_sided", "(q - kv) <= window", "abs(q - kv) <= window",
+     [lambda: pins.test_oracle_matches_brute_force("sliding_window2", "none"),
+      lambda: pins.test_oracle_matches_sdpa_boolean_masks(16, "window")]),
+    ("attended_count_ragged_chunk", "qi = np.arange(r0, min(Sq, r0 + chunk), dtype=np.int64)[:, None]",
+     "qi = np.arange(r0, r0 + chunk, dtype=np.int64)[:, None]",
+     [lambda: pins.test_attended_count_closed_forms(64)]),
     ("ragged_area", "area = (q1 - q0) * (k1 - k0)", "area = block * block",
      [lambda: pins.test_block_classes_brute_force(37, 50, "none")]),
     ("descending_lists", "cols = np.nonzero(flat_sel[r])[0]", "cols = np.nonzero(flat_sel[r])[0][::-1]",

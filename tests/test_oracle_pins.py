@@ -99,21 +99,26 @@ _LEN = np.array([5, 0], dtype=np.int32)
 _BIAS = gen._normal_bf16([99, 16], (2, 4, 7, 9), 0.5)
 _SLOPES = [0.5, 0.25, 0.125, 0.0625]
 
+# name -> (builder of the oracle functor, scalar brute-force functor).  The oracle
+# functors are built when a pin runs, so a pin exercised by the mutation tests
+# sees the mutated oracle module.
 MASKS = {
-    "none": (None, None),
-    "causal": (fo.causal(), lambda b, h, i, j: i >= j),
-    "sliding_causal2": (fo.sliding_causal(2), lambda b, h, i, j: i >= j and i - j <= 2),
-    "document": (fo.document(_DOC), lambda b, h, i, j: _DOC[b, i] == _DOC[b, j]),
-    "document_causal": (fo.document_causal(_DOC), lambda b, h, i, j: _DOC[b, i] == _DOC[b, j] and i >= j),
-    "prefix_lm3": (fo.prefix_lm(3), lambda b, h, i, j: j < 3 or i >= j),
-    "kv_len": (fo.kv_length(_LEN), lambda b, h, i, j: j < _LEN[b]),
+    "none": (lambda: None, None),
+    "causal": (lambda: fo.causal(), lambda b, h, i, j: i >= j),
+    "sliding_causal2": (lambda: fo.sliding_causal(2), lambda b, h, i, j: i >= j and i - j <= 2),
+    # the window term alone keeps every later key (j > i): only i - j <= 2 is required
+    "sliding_window2": (lambda: fo.sliding_window(2), lambda b, h, i, j: i - j <= 2),
+    "document": (lambda: fo.document(_DOC), lambda b, h, i, j: _DOC[b, i] == _DOC[b, j]),
+    "document_causal": (lambda: fo.document_causal(_DOC), lambda b, h, i, j: _DOC[b, i] == _DOC[b, j] and i >= j),
+    "prefix_lm3": (lambda: fo.prefix_lm(3), lambda b, h, i, j: j < 3 or i >= j),
+    "kv_len": (lambda: fo.kv_length(_LEN), lambda b, h, i, j: j < _LEN[b]),
 }
 MODS = {
-    "none": (None, None),
-    "alibi": (fo.alibi(_SLOPES), lambda s, b, h, i, j: s + _SLOPES[h] * (j - i)),
-    "softcap": (fo.softcap(0.7), lambda s, b, h, i, j: 0.7 * math.tanh(s / 0.7)),
-    "rel_pos": (fo.rel_pos(), lambda s, b, h, i, j: s + (i - j)),
-    "bias": (fo.bias(_BIAS), lambda s, b, h, i, j: s + _f(_BIAS[b, h, i, j])),
+    "none": (lambda: None, None),
+    "alibi": (lambda: fo.alibi(_SLOPES), lambda s, b, h, i, j: s + _SLOPES[h] * (j - i)),
+    "softcap": (lambda: fo.softcap(0.7), lambda s, b, h, i, j: 0.7 * math.tanh(s / 0.7)),
+    "rel_pos": (lambda: fo.rel_pos(), lambda s, b, h, i, j: s + (i - j)),
+    "bias": (lambda: fo.bias(_BIAS), lambda s, b, h, i, j: s + _f(_BIAS[b, h, i, j])),
 }
 
 
@@ -121,8 +126,8 @@ MODS = {
 @pytest.mark.parametrize("sname", list(MODS))
 def test_oracle_matches_brute_force(mname, sname):
     q, k, v = _tiny(7)
-    om, bm = MASKS[mname]
-    os_, bs = MODS[sname]
+    om, bm = MASKS[mname][0](), MASKS[mname][1]
+    os_, bs = MODS[sname][0](), MODS[sname][1]
     scale = 1.0 / math.sqrt(8)
     O, L = fo.attention(q, k, v, om, os_)
     Ob, Lb = brute_attention(q, k, v, bm, bs, scale)
@@ -153,13 +158,13 @@ def _sdpa(q, k, v, attn_mask, Hq, Hkv):
 
 
 @pytest.mark.parametrize("D", [16, 64])
-@pytest.mark.parametrize("case", ["causal", "sliding", "document", "prefix", "none"])
+@pytest.mark.parametrize("case", ["causal", "sliding", "window", "document", "prefix", "none"])
 def test_oracle_matches_sdpa_boolean_masks(D, case):
     B, Hq, Hkv, S = 2, 4, 2, 150
     q, k, v = gen.qkv(11, B, Hq, Hkv, S, S, D)
     docs = gen.document_ids(5, B, S, 20, 60)
-    om = {"causal": fo.causal(), "sliding": fo.sliding_causal(17), "document": fo.document_causal(docs),
-          "prefix": fo.prefix_lm(40), "none": None}[case]
+    om = {"causal": fo.causal(), "sliding": fo.sliding_causal(17), "window": fo.sliding_window(17),
+          "document": fo.document_causal(docs), "prefix": fo.prefix_lm(40), "none": None}[case]
     i = torch.arange(S)[:, None]
     j = torch.arange(S)[None, :]
     dt = torch.from_numpy(docs)
@@ -167,6 +172,8 @@ def test_oracle_matches_sdpa_boolean_masks(D, case):
         tm = (i >= j)[None, None]
     elif case == "sliding":
         tm = ((i >= j) & (i - j <= 17))[None, None]
+    elif case == "window":
+        tm = (i - j <= 17)[None, None]
     elif case == "document":
         tm = ((dt[:, :, None] == dt[:, None, :]) & (i >= j)[None])[:, None]
     elif case == "prefix":
@@ -238,7 +245,7 @@ def test_uniform_v_gives_constant_output(mname, sname):
     q, k, v = _tiny(21)
     c = gen.f32_to_bf16_bits(np.linspace(-2, 3, 8).astype(np.float32))
     v = np.broadcast_to(c, v.shape).copy()
-    O, _ = fo.attention(q, k, v, MASKS[mname][0], MODS[sname][0])
+    O, _ = fo.attention(q, k, v, MASKS[mname][0](), MODS[sname][0]())
     np.testing.assert_allclose(O, np.broadcast_to(fo.bf16_to_f64(c), O.shape), rtol=0, atol=1e-12)
 
 
@@ -246,7 +253,7 @@ def test_uniform_v_gives_constant_output(mname, sname):
 def test_causal_row0_is_v0(sname):
     B, H, S, D = 2, 4, 40, 16
     q, k, v = gen.qkv(22, B, H, H, S, S, D)
-    O, _ = fo.attention(q, k, v, fo.causal(), MODS[sname][0] if sname != "alibi" else fo.alibi(_SLOPES))
+    O, _ = fo.attention(q, k, v, fo.causal(), MODS[sname][0]() if sname != "alibi" else fo.alibi(_SLOPES))
     np.testing.assert_array_equal(O[:, :, 0], fo.bf16_to_f64(v[:, :, 0]))
 
 
@@ -480,6 +487,31 @@ def test_kv_length_tile_rule():
             assert cls[b, 0, 0, kb] == want
 
 
+@pytest.mark.parametrize("chunk", [64, 1024])
+def test_attended_count_closed_forms(chunk):
+    """N_att, the number of attended (b, h, q, kv) positions, against closed forms:
+    causal S(S+1)/2 per head, the sliding causal window min(q, W) + 1 per row, a
+    document-causal mask sum L(L+1)/2 over its documents, the kv_len prefix
+    Sq * len[b] per head; chunk sizes that do and do not divide S."""
+    B, H, S, W = 2, 3, 300, 37
+    assert fo.attended_count(fo.causal(), B, H, S, S, chunk) == B * H * S * (S + 1) // 2
+    assert fo.attended_count(fo.sliding_causal(W), B, H, S, S, chunk) == \
+        B * H * sum(min(q, W) + 1 for q in range(S))
+    assert fo.attended_count(None, B, H, S, 170, chunk) == B * H * S * 170
+    docs = gen.document_ids(41, B, S, 20, 90)
+    want = H * sum(int(L) * (int(L) + 1) // 2 for b in range(B) for L in np.bincount(docs[b]))
+    assert fo.attended_count(fo.document_causal(docs), B, H, S, S, chunk) == want
+    lens = np.array([0, 123], dtype=np.int32)
+    assert fo.attended_count(fo.kv_length(lens), B, H, 5, 200, chunk) == H * 5 * 123
+
+
+@pytest.mark.parametrize("mname", ["sliding_window2", "prefix_lm3", "document"])
+def test_attended_count_brute_force(mname):
+    om, bm = MASKS[mname][0](), MASKS[mname][1]
+    want = sum(1 for b in range(2) for h in range(4) for i in range(7) for j in range(9) if bm(b, h, i, j))
+    assert fo.attended_count(om, 2, 4, 7, 9, chunk=3) == want
+
+
 def test_blockmask_memory_ratio():
     # Paper review §4.1: one entry per 128x128 tile instead of per position -> 16384x fewer
     S = 8192
@@ -502,7 +534,7 @@ def test_backward_matches_finite_differences(mname, sname):
     """Central differences of L = sum(O * dO) with respect to sampled entries of
     Q, K and V (float64 inputs, tiny GQA shapes), against the analytic gradients."""
     q, k, v = (fo.bf16_to_f64(x) for x in _tiny(7))
-    om, sm = MASKS[mname][0], MODS[sname][0]
+    om, sm = MASKS[mname][0](), MODS[sname][0]()
     scale = 1.0 / math.sqrt(8)
     rng = np.random.default_rng([21, len(mname), len(sname)])
     dO = rng.standard_normal(q.shape)
