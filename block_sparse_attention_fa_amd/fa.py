@@ -117,11 +117,32 @@ def _check(status: int):
         raise FAError(status, f"{L.fa_status_string(status).decode()}: {L.fa_last_error().decode()}")
 
 
-def _stream(stream):
+def _torch_stream(stream):
+    """The stream a call runs on as a torch stream object: the current stream for
+    None, a torch stream as given, or a raw hipStream_t handle wrapped."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _stream(stream):
+    return c_void_p(_torch_stream(stream).cuda_stream)
+
+
+def _on(stream):
+    """Context in which the binding allocates what a call writes (outputs it
+    creates, workspaces): the call's own stream, so the caching allocator never
+    hands that memory to other work while the call's kernels still use it."""
+    import torch
+    return torch.cuda.stream(_torch_stream(stream))
+
+
+def _need(cond, msg):
+    if not cond:
+        raise FAError(FA_ERR_SHAPE, msg)
 
 
 def _ptr(t):
@@ -137,6 +158,29 @@ class MaskMod:
         self.kind = MASK_KINDS[kind] if isinstance(kind, str) else int(kind)
         self.window, self.prefix_len = int(window), int(prefix_len)
         self.doc_ids, self.kv_len = doc_ids, kv_len
+
+    def check(self, B, Sq, Skv):
+        """What the C ABI cannot see behind the raw pointers: dtype, layout, length
+        and device of doc_ids ([S] or [1 or >= B, S] int32, unit stride along
+        tokens, S >= max(Sq, Skv)) and kv_len ([>= B] int32, contiguous).
+        Checks run dtype and shape first, device last.  Raises FAError(FA_ERR_SHAPE)."""
+        import torch
+        if self.kind in (MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL):
+            d = self.doc_ids
+            _need(d is not None, "a document mask needs doc_ids")
+            _need(d.dtype == torch.int32, f"doc_ids must be torch.int32 (got {d.dtype})")
+            _need(d.dim() in (1, 2) and d.stride(-1) == 1, "doc_ids must be [S] or [B, S] with unit stride along S")
+            _need(d.shape[-1] >= max(Sq, Skv), f"doc_ids has {d.shape[-1]} tokens, the call needs {max(Sq, Skv)}")
+            _need(d.dim() == 1 or d.shape[0] == 1 or d.shape[0] >= B,
+                  f"doc_ids has {d.shape[0]} batch rows, the call has B={B}")
+            _need(d.is_cuda, "doc_ids must be on the GPU")
+        if self.kind == MASK_KV_LEN:
+            t = self.kv_len
+            _need(t is not None, "a kv_len mask needs kv_len")
+            _need(t.dtype == torch.int32, f"kv_len must be torch.int32 (got {t.dtype})")
+            _need(t.dim() == 1 and t.stride(0) == 1, "kv_len must be a contiguous 1-d tensor")
+            _need(t.shape[0] >= B, f"kv_len has {t.shape[0]} entries, the call has B={B}")
+            _need(t.is_cuda, "kv_len must be on the GPU")
 
     def desc(self) -> MaskDesc:
         d = MaskDesc()
@@ -155,6 +199,27 @@ class ScoreMod:
     def __init__(self, kind="none", softcap=0.0, alibi_slopes=None, bias=None):
         self.kind = SCORE_KINDS[kind] if isinstance(kind, str) else int(kind)
         self.softcap, self.alibi_slopes, self.bias = float(softcap), alibi_slopes, bias
+
+    def check(self, B, Hq, Sq, Skv):
+        """What the C ABI cannot see: alibi_slopes must be a contiguous float32
+        tensor of >= Hq entries; bias a 4-d bfloat16 tensor whose dims are each 1
+        (broadcast) or at least (B, Hq, Sq, Skv), unit stride along keys.  Checks
+        run dtype and shape first, device last.  Raises FAError(FA_ERR_SHAPE)."""
+        import torch
+        if self.kind == SCORE_ALIBI and self.alibi_slopes is not None:
+            t = self.alibi_slopes
+            _need(t.dtype == torch.float32, f"alibi_slopes must be torch.float32 (got {t.dtype})")
+            _need(t.dim() == 1 and t.stride(0) == 1, "alibi_slopes must be a contiguous 1-d tensor")
+            _need(t.shape[0] >= Hq, f"alibi_slopes has {t.shape[0]} entries, the call has Hq={Hq}")
+            _need(t.is_cuda, "alibi_slopes must be on the GPU")
+        if self.kind == SCORE_BIAS:
+            t = self.bias
+            _need(t is not None, "a bias score needs a bias tensor")
+            _need(t.dtype == torch.bfloat16, f"bias must be torch.bfloat16 (got {t.dtype})")
+            _need(t.dim() == 4 and t.stride(3) == 1, "bias must be 4-d [B, H, Sq, Skv] with unit stride along keys")
+            for i, (n, want) in enumerate(zip(t.shape, (B, Hq, Sq, Skv))):
+                _need(n == 1 or n >= want, f"bias dim {i} has size {n}, the call needs 1 or >= {want}")
+            _need(t.is_cuda, "bias must be on the GPU")
 
     def desc(self) -> ScoreDesc:
         d = ScoreDesc()
@@ -263,7 +328,9 @@ def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, devi
                         transposed=False):
     """Allocate a BlockMask and build it on the device (asynchronously on `stream`);
     transposed=True also builds the per-KV-block view the backward needs."""
-    bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed)
+    mask.check(Bm, Sq, Skv)
+    with _on(stream):
+        bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed)
     _check(lib().fa_build_block_mask(ctypes.byref(bm.c), Sq, Skv, _stream(stream)))
     return bm
 
@@ -314,8 +381,12 @@ def _attn_args(q, k, v, out, lse, block_mask, score, scale, num_splits, page_tab
         a.page_table_stride = page_table.stride(0)
         a.num_pages = k.shape[0]
     a.scale = float(scale)
+    if block_mask is not None:
+        block_mask.mask.check(a.B, a.Sq, a.Skv)
+    score = score or ScoreMod()
+    score.check(a.B, a.Hq, a.Sq, a.Skv)
     a.block_mask = ctypes.pointer(block_mask.c) if block_mask is not None else None
-    a.score = (score or ScoreMod()).desc()
+    a.score = score.desc()
     a.num_splits = int(num_splits)
     return a
 
@@ -325,7 +396,9 @@ def fa_forward(q, k, v, block_mask: BlockMask | None = None, score: ScoreMod | N
     """O = softmax(mod(Q K^T * scale)) V for bf16 Q [B,Hq,Sq,D], K/V [B,Hkv,Skv,D]."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        _check_tensors(q, k, v, q, lse)  # before touching the device
+        with _on(stream):
+            out = torch.empty_like(q)
     a = _attn_args(q, k, v, out, lse, block_mask, score, scale, 0)
     _check(lib().fa_forward(ctypes.byref(a), _stream(stream)))
     return out
@@ -345,12 +418,15 @@ def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: S
     logical block j of sequence b is page page_table[b, j]."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        _check_tensors(q, k_cache, v_cache, q, lse, paged=page_table is not None)  # before touching the device
+        with _on(stream):
+            out = torch.empty_like(q)
     a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits, page_table)
     n = c_size_t()
     _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
-        workspace = torch.empty(max(1, n.value // 4), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            workspace = torch.empty(max(1, n.value // 4), dtype=torch.float32, device=q.device)
     _check(lib().fa_decode(ctypes.byref(a), c_void_p(workspace.data_ptr()),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
@@ -372,14 +448,16 @@ def fa_backward(q, k, v, out, lse, dout, block_mask: BlockMask | None = None, sc
     import torch
     if block_mask is not None and not block_mask.transposed:
         raise FAError(FA_ERR_NULL, "the backward needs a BlockMask built with transposed=True")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    if lse is None:
+        raise FAError(FA_ERR_NULL, "the backward needs the forward's lse")
+    _check_tensors(q, k, v, out, lse)  # before touching the device
+    with _on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(ref.shape) or not t.is_cuda:
             raise FAError(FA_ERR_SHAPE, f"{name} must be a torch.bfloat16 GPU tensor shaped {tuple(ref.shape)}")
-    if lse is None:
-        raise FAError(FA_ERR_NULL, "the backward needs the forward's lse")
     a = _attn_args(q, k, v, out, lse, block_mask, score, scale, 0)
     g = GradArgs()
     g.dout, g.dq, g.dk, g.dv = dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
@@ -390,7 +468,8 @@ def fa_backward(q, k, v, out, lse, dout, block_mask: BlockMask | None = None, sc
     n = c_size_t()
     _check(lib().fa_backward_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
-        workspace = torch.empty(max(4, n.value // 4), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            workspace = torch.empty(max(4, n.value // 4), dtype=torch.float32, device=q.device)
     _check(lib().fa_backward(ctypes.byref(a), ctypes.byref(g), c_void_p(workspace.data_ptr()),
                              workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv

@@ -275,3 +275,43 @@ def test_backward_validation_codes():
     a.block_mask = ctypes.pointer(bm)
     assert bwd(a, grads()) == fa.FA_ERR_NULL
     assert "transposed view" in L.fa_last_error().decode()
+
+
+def test_binding_rejects_bad_mask_and_score_tensors():
+    """doc_ids, kv_len, alibi_slopes and bias reach the kernels as bare pointers:
+    the binding checks their dtype, length and device before any call (dtype and
+    shape first, so these run without a GPU)."""
+    import torch
+    i32, bf = torch.int32, torch.bfloat16
+    B, Hq, S = 2, 4, 300
+    mask_cases = [
+        fa.MaskMod("document_causal", doc_ids=torch.zeros((B, S), dtype=torch.int64)),   # int64 ids
+        fa.MaskMod("document", doc_ids=torch.zeros((B, S - 1), dtype=i32)),               # too short
+        fa.MaskMod("document", doc_ids=torch.zeros((S, B), dtype=i32).t()),              # strided tokens
+        fa.MaskMod("document", doc_ids=None),
+        fa.MaskMod("document", doc_ids=torch.zeros((B, S), dtype=i32)),                   # host memory
+        fa.MaskMod("kv_len", kv_len=torch.full((B,), 7, dtype=torch.int64)),               # int64 lengths
+        fa.MaskMod("kv_len", kv_len=torch.full((B - 1,), 7, dtype=i32)),                   # too few
+        fa.MaskMod("kv_len", kv_len=torch.full((B,), 7, dtype=i32)),                       # host memory
+    ]
+    for m in mask_cases:
+        with pytest.raises(fa.FAError) as e:
+            fa.fa_build_block_mask(m, B, 1, S, S)
+        assert e.value.status == fa.FA_ERR_SHAPE
+    fa.MaskMod("causal").check(B, S, S)  # masks without tensors have nothing to check
+    score_cases = [
+        fa.ScoreMod("alibi", alibi_slopes=torch.ones(Hq, dtype=torch.float64)),
+        fa.ScoreMod("alibi", alibi_slopes=torch.ones(Hq - 1)),
+        fa.ScoreMod("alibi", alibi_slopes=torch.ones(Hq)),                                 # host memory
+        fa.ScoreMod("bias", bias=torch.zeros((B, Hq, S, S), dtype=torch.float32)),         # fp32 bias
+        fa.ScoreMod("bias", bias=torch.zeros((Hq, S, S), dtype=bf)),                       # 3-d
+        fa.ScoreMod("bias", bias=torch.zeros((B, Hq, S, S - 8), dtype=bf)),                # too few keys
+        fa.ScoreMod("bias", bias=torch.zeros((B, 2, S, S), dtype=bf)),                     # 2 of 4 heads
+        fa.ScoreMod("bias", bias=torch.zeros((1, 1, S, S), dtype=bf)),                     # host memory
+        fa.ScoreMod("bias"),
+    ]
+    for sm in score_cases:
+        with pytest.raises(fa.FAError) as e:
+            sm.check(B, Hq, S, S)
+        assert e.value.status == fa.FA_ERR_SHAPE
+    fa.ScoreMod("alibi").check(B, Hq, S, S)  # default slopes: nothing to check
