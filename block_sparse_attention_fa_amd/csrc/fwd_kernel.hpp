@@ -91,14 +91,15 @@ __device__ __forceinline__ uint32_t lds_address(const void* ptr) {
 // LDS reads comes from the volatile wait/barrier statements around it, which
 // do clobber memory and which volatile asm cannot be reordered with.
 // dma16: 64-bit per-lane address.  dma16s: uniform 64-bit base + 32-bit
-// per-lane byte offset (one VGPR per lane).
+// per-lane byte offset (one VGPR per lane).  Both set M0 (the LDS base of the
+// DMA), which is declared clobbered.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(lds));
+               :: "v"(gaddr), "s"(lds) : "m0");
 }
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds));
+               :: "v"(voff), "s"(sbase), "s"(lds) : "m0");
 }
 
 // LDS swizzles (16-byte chunk index XOR a function of the row), chosen per
