@@ -1,6 +1,8 @@
 // Split-KV decode with a log-sum-exp merge.
 //
-// One query token per sequence against a long KV cache.  Following the
+// One query token per sequence against a long KV cache; the token of
+// sequence b sits at position q_pos[b] (0 without q_pos), which the
+// score_mods see as its q index.  Following the
 // "Flex Decoding" part of the talk summary "FlexAttention: A Flexible and
 // Performant Approach to Transformer Attention", the key axis is split into
 // chunks that are processed in parallel and combined by a final reduction;
@@ -140,9 +142,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)(hkv * G + g) * p.qs[1];
     unpack8(*(const u32x4_t*)(Qp + 8 * sub), qf[g]);
   }
+  // the query's position in its sequence: the q index the mods see
+  const int qpos = P.q_pos != nullptr ? P.q_pos[b] : 0;
   typename Score::Row srow[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) srow[g] = Score::row(p.score, b, hkv * G + g, 0);
+  for (int g = 0; g < G; ++g) srow[g] = Score::row(p.score, b, hkv * G + g, qpos);
   __syncthreads();
 
   // An iteration covers STEP consecutive rows of the chunk (inside one tile):
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
       }
       bool keep = kv < p.Skv;
       if (keep && part) {
-        EvalMask em{p.mask, b, hkv * G, 0, kv, false};
+        EvalMask em{p.mask, b, hkv * G, qpos, kv, false};
         dispatch_mask(P.mask_kind, em);
         keep = em.result;
       }

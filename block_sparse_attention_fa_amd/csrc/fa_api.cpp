@@ -81,6 +81,7 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
   if (a->Hq % a->Hkv != 0) return fail(FA_ERR_SHAPE, "Hq %% Hkv != 0 (%d, %d)", a->Hq, a->Hkv);
   if (a->D != 64 && a->D != 128) return fail(FA_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", a->D);
   if (decode && a->Sq != 1) return fail(FA_ERR_SHAPE, "decode needs Sq == 1 (got %d)", a->Sq);
+  if (!decode && a->q_pos != nullptr) return fail(FA_ERR_UNSUPPORTED, "q_pos is an argument of fa_decode only");
   if (a->page_table != nullptr) {
     if (!decode) return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is supported by fa_decode only");
     if (a->num_pages <= 0) return fail(FA_ERR_SHAPE, "num_pages must be positive (got %d)", a->num_pages);
@@ -213,6 +214,12 @@ fa_status prepare_decode(const fa_attn_args* a, FwdParams& p, int& mask_kind, De
     return fail(FA_ERR_UNSUPPORTED, "decode GQA group %d (supported: 1, 2, 4, 8)", G);
   if (a->block_mask && a->block_mask->Hm > 1 && G != 1)
     return fail(FA_ERR_UNSUPPORTED, "decode with a per-head BlockMask needs group size 1");
+  // The decode BlockMask has one query row (built with Sq = 1, the query at
+  // index 0), so a mask that depends on the query position would be
+  // classified for the wrong query; kv_len expresses a causal cache.
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_KV_LEN)
+    return fail(FA_ERR_UNSUPPORTED, "decode supports the none and kv_len masks only (got kind %d): the "
+                                    "BlockMask's one query row cannot follow the query position", mask_kind);
   if (a->num_splits < 0) return fail(FA_ERR_SHAPE, "num_splits < 0");
   plan = decode_plan(a);
   if ((long long)plan.splits > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "too many splits");
@@ -400,6 +407,7 @@ fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_byt
   P.page_table = a->page_table;
   P.pt_stride = a->page_table_stride;
   P.num_pages = a->num_pages;
+  P.q_pos = a->q_pos;
   st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, (hipStream_t)stream);
   if (st != FA_OK) return fail(st, "decode launch failed");
   return FA_OK;
@@ -431,6 +439,22 @@ fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* worksp
   st = launch_backward(a->D, mask_kind, a->score.kind, P, (hipStream_t)stream);
   if (st != FA_OK) return fail(st, "backward launch failed");
   return FA_OK;
+}
+
+fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, float* sink, double* flops, void* stream) {
+  if (sink == nullptr || flops == nullptr) return fail(FA_ERR_NULL, "sink and flops must be non-NULL");
+  if (workgroups < 1 || iterations < 1) return fail(FA_ERR_SHAPE, "workgroups and iterations must be >= 1");
+  *flops = probe_mfma_flops(workgroups, iterations);
+  const fa_status st = launch_probe_mfma(workgroups, iterations, sink, (hipStream_t)stream);
+  return st == FA_OK ? FA_OK : fail(st, "MFMA probe launch failed");
+}
+
+fa_status fa_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr) return fail(FA_ERR_NULL, "src and dst must be non-NULL");
+  if (bytes == 0 || bytes % 16 != 0) return fail(FA_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned16(src) || !aligned16(dst)) return fail(FA_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+  const fa_status st = launch_probe_copy(src, dst, bytes, (hipStream_t)stream);
+  return st == FA_OK ? FA_OK : fail(st, "copy probe launch failed");
 }
 
 }  // extern "C"

@@ -65,6 +65,7 @@ struct DecodeParams {
   const int* page_table;  // nullptr: per-sequence caches; else page of (b, logical block)
   long long pt_stride;    // page-table entries between sequences
   int num_pages;
+  const int* q_pos;       // nullptr: query position 0; else position of sequence b's query
 };
 
 struct BwdParams {
@@ -99,6 +100,9 @@ struct BuildParams {
 };
 
 fa_status launch_block_mask(int mask_kind, const BuildParams& p, hipStream_t stream);
+fa_status launch_probe_mfma(int workgroups, int iterations, float* sink, hipStream_t stream);
+double probe_mfma_flops(int workgroups, int iterations);
+fa_status launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 fa_status launch_forward(int D, int mask_kind, int score_kind, const FwdParams& p, hipStream_t stream);
 // One translation unit per mask kind (compiled in parallel).
 fa_status launch_forward_none(int D, int score_kind, const FwdParams& p, hipStream_t stream);

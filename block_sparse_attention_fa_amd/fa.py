@@ -62,7 +62,8 @@ class AttnArgs(ctypes.Structure):
                 ("B", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("Sq", c_int32), ("Skv", c_int32),
                 ("D", c_int32), ("scale", c_float), ("block_mask", POINTER(BlockMaskC)),
                 ("score", ScoreDesc), ("num_splits", c_int32),
-                ("page_table", c_void_p), ("page_table_stride", c_int64), ("num_pages", c_int32)]
+                ("page_table", c_void_p), ("page_table_stride", c_int64), ("num_pages", c_int32),
+                ("q_pos", c_void_p)]
 
 
 class GradArgs(ctypes.Structure):
@@ -83,6 +84,8 @@ SIGNATURES = {
     "fa_decode": (c_int32, [POINTER(AttnArgs), c_void_p, c_size_t, c_void_p]),
     "fa_backward_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
     "fa_backward": (c_int32, [POINTER(AttnArgs), POINTER(GradArgs), c_void_p, c_size_t, c_void_p]),
+    "fa_probe_mfma": (c_int32, [c_int32, c_int32, c_void_p, POINTER(ctypes.c_double), c_void_p]),
+    "fa_probe_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 
@@ -412,16 +415,25 @@ def fa_decode_workspace_size(q, k, v, block_mask=None, score=None, num_splits=0,
 
 
 def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
-              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None, page_table=None):
+              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None, page_table=None,
+              q_pos=None):
     """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D], or, with an int32
     page_table [B, blocks], against page pools [num_pages, Hkv, 128, D] where
-    logical block j of sequence b is page page_table[b, j]."""
+    logical block j of sequence b is page page_table[b, j].  q_pos (int32 [B],
+    optional) is each query token's position, the q index the score_mods see
+    (0 when not given); pass kv_len - 1 for the newest token of a causal cache."""
     import torch
+    if q_pos is not None:
+        _need(q_pos.dtype == torch.int32 and q_pos.dim() == 1 and q_pos.stride(0) == 1,
+              "q_pos must be a contiguous 1-d torch.int32 tensor")
+        _need(q_pos.shape[0] >= q.shape[0], f"q_pos has {q_pos.shape[0]} entries, the call has B={q.shape[0]}")
+        _need(q_pos.is_cuda, "q_pos must be on the GPU")
     if out is None:
         _check_tensors(q, k_cache, v_cache, q, lse, paged=page_table is not None)  # before touching the device
         with _on(stream):
             out = torch.empty_like(q)
     a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits, page_table)
+    a.q_pos = q_pos.data_ptr() if q_pos is not None else None
     n = c_size_t()
     _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
@@ -473,3 +485,25 @@ def fa_backward(q, k, v, out, lse, dout, block_mask: BlockMask | None = None, sc
     _check(lib().fa_backward(ctypes.byref(a), ctypes.byref(g), c_void_p(workspace.data_ptr()),
                              workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv
+
+
+# --- measurement probes ------------------------------------------------------------
+
+def fa_probe_mfma(workgroups, iterations, sink, stream=None):
+    """Launch the bf16 MFMA loop (include/fa.h); returns its flop count.
+    sink: float32 GPU tensor of >= workgroups * 256 elements."""
+    import torch
+    _need(sink.dtype == torch.float32 and sink.is_cuda and sink.numel() >= workgroups * 256,
+          "sink must be a float32 GPU tensor of >= workgroups * 256 elements")
+    flops = ctypes.c_double()
+    _check(lib().fa_probe_mfma(int(workgroups), int(iterations), c_void_p(sink.data_ptr()), ctypes.byref(flops),
+                               _stream(stream)))
+    return flops.value
+
+
+def fa_probe_copy(src, dst, stream=None):
+    """Streaming copy of src's bytes into dst (GPU tensors of equal byte size)."""
+    n = src.numel() * src.element_size()
+    _need(src.is_cuda and dst.is_cuda and dst.numel() * dst.element_size() == n and src.is_contiguous()
+          and dst.is_contiguous(), "src and dst must be contiguous GPU tensors of the same byte size")
+    _check(lib().fa_probe_copy(c_void_p(src.data_ptr()), c_void_p(dst.data_ptr()), n, _stream(stream)))

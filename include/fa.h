@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 #define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
 
 typedef enum {
@@ -167,6 +167,12 @@ typedef struct {
   const int32_t* page_table;  /* device int32, >= B rows of page_table_stride entries */
   int64_t page_table_stride;  /* entries between sequences, >= ceil(Skv / FA_BLOCK) */
   int32_t num_pages;          /* pages in each pool */
+  /* fa_decode only: the position of each sequence's query token, the q index
+   * the score_mods see (talk summary, "Flex Decoding": the score_mod still
+   * applies; Concepts "score_mod": ALiBi reads q_idx).  Device int32 [B], or
+   * NULL for position 0 in every sequence.  For a cache holding len[b] tokens
+   * and the newest token as query, pass len[b] - 1.  fa_forward requires NULL. */
+  const int32_t* q_pos;
 } fa_attn_args;
 
 /* Backward pass: the gradient buffers.  Strides are in elements for (b, h, s, d),
@@ -224,7 +230,11 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
 
 /* Split-KV decode (talk summary, "Flex Decoding": split along the key axis
  * for parallelism, then a final reduction; score_mod still applies).  Sq must
- * be 1; the query sits at q index 0.  Each sequence's block list (its
+ * be 1; the query of sequence b sits at q index q_pos[b] (0 when q_pos is
+ * NULL), which is the q the score_mods see.  The BlockMask is the one-row
+ * BlockMask of the KV axis (built with Sq = 1), so its mask must not depend on
+ * the query position: only FA_MASK_NONE and FA_MASK_KV_LEN are accepted (a
+ * causal cache of len[b] tokens is kv < len[b]).  Each sequence's block list (its
  * BlockMask row) is dealt round-robin into chunks (chunk s holds entries s,
  * s + splits, s + 2 splits, ...); one workgroup per (chunk, KV head, batch
  * row) computes all Hq/Hkv query heads of that KV head against the chunk, and
@@ -236,7 +246,8 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
  * With a page table (see fa_attn_args) the K/V rows of each listed block are
  * read from its page; the arithmetic is otherwise unchanged.
  * Errors: as fa_forward, plus FA_ERR_SHAPE for Sq != 1, num_pages <= 0 or
- * page_table_stride < ceil(Skv / FA_BLOCK), and FA_ERR_WORKSPACE. */
+ * page_table_stride < ceil(Skv / FA_BLOCK), FA_ERR_UNSUPPORTED for a mask kind
+ * other than NONE / KV_LEN, and FA_ERR_WORKSPACE. */
 fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host only.  Bytes of workspace fa_backward needs: two fp32 values (base-2
@@ -262,6 +273,26 @@ fa_status fa_backward_workspace_size(const fa_attn_args* a, size_t* bytes);
  * transposed view missing) and FA_ERR_WORKSPACE. */
 fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* ---- Measurement probes (not part of the attention path) ----------------
+ * Kernels whose rate is what the chip reaches in practice, so that a kernel's
+ * throughput can be given as a fraction of a measured peak beside the
+ * published one (bf16 matrix peak, HBM bandwidth). */
+
+/* Dense bf16 MFMA loop: `workgroups` workgroups of 256 threads; every wave runs
+ * `iterations` rounds of 8 independent v_mfma_f32_32x32x16_bf16 chains on
+ * register operands (32768 flops per instruction).  *flops receives the flop
+ * count of the launch; `sink` (device fp32, workgroups * 256 entries) receives
+ * one value per lane so the work is not optimised away.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (workgroups or iterations < 1), FA_ERR_HIP. */
+fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, float* sink, double* flops, void* stream);
+
+/* Streaming copy of `bytes` bytes from src to dst (device pointers, 16-byte
+ * aligned, bytes a multiple of 16): 16-byte loads and stores, each byte read
+ * and written once.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (bytes 0 or not a multiple of 16),
+ * FA_ERR_UNSUPPORTED (alignment), FA_ERR_HIP. */
+fa_status fa_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

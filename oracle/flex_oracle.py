@@ -262,18 +262,30 @@ def attention(q, k, v, mask_mod=None, score_mod=None, scale=None, chunk=1024):
     return O, L
 
 
-def decode(q, k_cache, v_cache, lengths, score_mod=None, scale=None, extra_mask=None):
+def decode(q, k_cache, v_cache, lengths, score_mod=None, scale=None, extra_mask=None, positions=None):
     """One query token per sequence against a KV cache (talk summary, Flex Decoding).
 
-    q: [B,Hq,1,D]; caches: [B,Hkv,KV,D]; lengths: int [B].  The query sits at
-    q_idx = 0 and the only mask is kv < lengths[b] (AND extra_mask if given).
-    The split-K + final reduction of the talk is an execution strategy that
-    reaches this same value, so the oracle computes it directly.
+    q: [B,Hq,1,D]; caches: [B,Hkv,KV,D]; lengths: int [B]; positions: int [B]
+    or None.  The query token of sequence b sits at position positions[b] (0
+    when not given): that is the q_idx its mask_mod and score_mod see (the talk
+    keeps the score_mod in decoding; Concepts "score_mod": ALiBi reads q_idx).
+    The only mask is kv < lengths[b] (AND extra_mask if given).  The split-K +
+    final reduction of the talk is an execution strategy that reaches this same
+    value, so the oracle computes it directly.
     """
+    pos = np.zeros(q.shape[0], dtype=np.int64) if positions is None else np.asarray(positions, dtype=np.int64)
     mask = kv_length(lengths)
     if extra_mask is not None:
         mask = and_masks(mask, extra_mask)
-    return attention(q, k_cache, v_cache, mask_mod=mask, score_mod=score_mod, scale=scale)
+
+    def mask_at(b, h, qi, kv):       # row 0 of the one-token query is position pos[b]
+        return mask(b, h, qi + pos[b], kv)
+
+    mod_at = None
+    if score_mod is not None:
+        def mod_at(s, b, h, qi, kv):
+            return score_mod(s, b, h, qi + pos[b], kv)
+    return attention(q, k_cache, v_cache, mask_mod=mask_at, score_mod=mod_at, scale=scale)
 
 
 # ---------------------------------------------------------------------------

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 2
+    assert L.fa_abi_version() == 3
     for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                                  "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
         assert L.fa_status_string(code).decode() == name
@@ -315,3 +315,38 @@ def test_binding_rejects_bad_mask_and_score_tensors():
             sm.check(B, Hq, S, S)
         assert e.value.status == fa.FA_ERR_SHAPE
     fa.ScoreMod("alibi").check(B, Hq, S, S)  # default slopes: nothing to check
+
+
+def test_decode_accepts_only_position_free_masks_and_forward_rejects_q_pos():
+    """The decode BlockMask has one query row built at q index 0, so fa_decode
+    takes only the masks that do not look at the query position (none, kv_len);
+    q_pos belongs to fa_decode alone."""
+    n = ctypes.c_size_t()
+    for kind in range(fa.MASK_KV_LEN + 1):
+        a = _args(B=1, Hq=2, Hkv=2, Sq=1, Skv=512, D=128)
+        b = _bm(kind=kind, Sq=1, Skv=512, NQ=1, NK=4)
+        b.mask.kv_len = b.mask.doc_ids = 0x10000
+        if kind in (fa.MASK_DOCUMENT, fa.MASK_DOCUMENT_CAUSAL):
+            continue  # already rejected for Sq != Skv
+        a.block_mask = ctypes.pointer(b)
+        st = fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        want = fa.FA_OK if kind in (fa.MASK_NONE, fa.MASK_KV_LEN) else fa.FA_ERR_UNSUPPORTED
+        assert st == want, (kind, st)
+        if st != fa.FA_OK:
+            assert "query" in fa.lib().fa_last_error().decode()
+    a = _args(Sq=1)
+    a.q_pos = 0x10000
+    assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    assert _status(a) == fa.FA_ERR_UNSUPPORTED  # fa_forward
+
+
+def test_probe_validation_codes():
+    L = fa.lib()
+    f = ctypes.c_double()
+    assert L.fa_probe_mfma(1, 1, None, ctypes.byref(f), None) == fa.FA_ERR_NULL
+    assert L.fa_probe_mfma(0, 1, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_mfma(1, 0, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_copy(None, 0x10000, 16, None) == fa.FA_ERR_NULL
+    assert L.fa_probe_copy(0x10000, 0x20000, 0, None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_copy(0x10000, 0x20000, 24, None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_copy(0x10008, 0x20000, 32, None) == fa.FA_ERR_UNSUPPORTED

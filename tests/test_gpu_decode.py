@@ -173,3 +173,27 @@ def test_paged_decode(G, D, score, share):
     C.compare(got, O, "paged decode")
     C.compare_lse(lse.cpu().numpy()[..., 0], L[..., 0], "paged decode")
     assert torch.equal(out, out_c) and torch.equal(lse, lse_c)
+
+
+@pytest.mark.parametrize("score", ["alibi", "rel_pos", "softcap"])
+def test_decode_at_query_positions(score):
+    """The query of sequence b at position q_pos[b] (the newest token of its cache,
+    or any other position): the score_mods see that q index, so ALiBi and the
+    relative position shift every score of the row, which the LSE shows."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    B, Hq, Hkv, KV, D = 4, 8, 2, 1500, 128
+    print(f"[case] decode at query positions, score={score}", flush=True)
+    q = gen.qkv(57, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(58, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([1500, 700, 129, 1], dtype=np.int32)
+    pos = np.array([1499, 699, 4000, 0], dtype=np.int32)
+    spec = C.make_spec(59, "kv_len", score, B, Hq, 1, KV, cap=50.0)
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    out = fa.fa_decode(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm,
+                       score=C.gpu_score(spec), lse=lse, q_pos=torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    O, L = fo.decode(q, k, v, lens, C.oracle_score(spec, Hq), positions=pos)
+    C.compare(gen.bf16_bits_to_f32(gen.from_torch_bf16(out)), O, f"decode q_pos {score}")
+    C.compare_lse(lse.cpu().numpy()[..., 0], L[..., 0], f"decode q_pos {score}")

@@ -44,6 +44,9 @@ MUTANTS = [
     ("attended_count_ragged_chunk", "qi = np.arange(r0, min(Sq, r0 + chunk), dtype=np.int64)[:, None]",
      "qi = np.arange(r0, r0 + chunk, dtype=np.int64)[:, None]",
      [lambda: pins.test_attended_count_closed_forms(64)]),
+    ("decode_mod_ignores_position", "return score_mod(s, b, h, qi + pos[b], kv)", "return score_mod(s, b, h, qi, kv)",
+     [lambda: pins.test_decode_at_query_positions_matches_sdpa("alibi"),
+      pins.test_decode_at_position_p_is_row_p_of_the_causal_forward]),
     ("ragged_area", "area = (q1 - q0) * (k1 - k0)", "area = block * block",
      [lambda: pins.test_block_classes_brute_force(37, 50, "none")]),
     ("descending_lists", "cols = np.nonzero(flat_sel[r])[0]", "cols = np.nonzero(flat_sel[r])[0][::-1]",

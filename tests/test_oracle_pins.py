@@ -387,6 +387,52 @@ def test_decode_equals_single_row_sdpa():
             np.testing.assert_allclose(O[b, h, 0], (w @ V) / w.sum(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("mod", ["alibi", "rel_pos"])
+def test_decode_at_query_positions_matches_sdpa(mod):
+    """A decode query at position p sees q_idx = p: ALiBi adds slope[h] (kv - p),
+    the relative position (p - kv); torch SDPA with that additive mask."""
+    B, Hq, Hkv, KV, D = 3, 4, 2, 200, 16
+    q = gen.qkv(33, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(34, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([200, 77, 1], dtype=np.int32)
+    pos = np.array([199, 500, 0], dtype=np.int64)     # a position need not be inside the cache
+    slopes = fo.default_alibi_slopes(Hq)
+    sm = fo.alibi(slopes) if mod == "alibi" else fo.rel_pos()
+    O, L = fo.decode(q, k, v, lens, sm, positions=pos)
+    kv = np.arange(KV, dtype=np.float64)
+    for b in range(B):
+        if mod == "alibi":
+            add = slopes[:, None] * (kv[None, :] - pos[b])          # [Hq, KV]
+        else:
+            add = np.broadcast_to(pos[b] - kv[None, :], (Hq, KV))
+        am = np.where(kv[None, :] < lens[b], add, -np.inf)[:, None, :]   # [Hq, 1, KV]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            _t(q[b:b + 1]), _t(k[b:b + 1]), _t(v[b:b + 1]), attn_mask=torch.from_numpy(am)[None],
+            enable_gqa=True).numpy()
+        np.testing.assert_allclose(O[b:b + 1], ref, rtol=0, atol=1e-12)
+        # A position shifts every score of the row by the same amount, so O alone
+        # cannot show it; the log-sum-exp does.
+        hk = np.arange(Hq) // (Hq // Hkv)
+        sc = (_t(q[b, :, 0])[:, None, :] * _t(k[b, hk])).sum(-1) / math.sqrt(D)   # [Hq, KV]
+        lse = torch.logsumexp(sc + torch.from_numpy(am[:, 0, :]), dim=-1).numpy()
+        np.testing.assert_allclose(L[b, :, 0], lse, rtol=0, atol=1e-12)
+
+
+def test_decode_at_position_p_is_row_p_of_the_causal_forward():
+    B, H, S, D, p = 2, 4, 90, 16, 61
+    q, k, v = gen.qkv(35, B, H, H, S, S, D)
+    sm = fo.alibi(fo.default_alibi_slopes(H))
+    O, L = fo.attention(q, k, v, fo.causal(), sm)
+    Od, Ld = fo.decode(q[:, :, p:p + 1], k, v, np.full(B, p + 1, dtype=np.int32), sm, positions=np.full(B, p))
+    np.testing.assert_allclose(Od[:, :, 0], O[:, :, p], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Ld[:, :, 0], L[:, :, p], rtol=0, atol=1e-12)
+    # the same query at position 0: same output, LSE lower by slope[h] * p (softmax ignores a constant)
+    O0, L0 = fo.decode(q[:, :, p:p + 1], k, v, np.full(B, p + 1, dtype=np.int32), sm)
+    np.testing.assert_allclose(O0, Od, rtol=0, atol=1e-12)
+    slopes = fo.default_alibi_slopes(H)[None, :, None]
+    np.testing.assert_allclose(Ld, L0 - slopes * p, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # BlockMask
 # ---------------------------------------------------------------------------
