@@ -88,6 +88,17 @@ def test_every_tile_listed_as_partial(mask):
     C.compare_lse(lse.cpu().numpy(), L, f"every tile {mask}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,score,dense", [("none", "alibi", False), ("prefix_lm", "softcap", False),
+                                              ("none", "rel_pos", True)])
+def test_block_lists_longer_than_the_register_window(mask, score, dense, D):
+    """Rows that list 157 tiles (prefix_lm with prefix 20000) or 258 (no mask, and
+    the dense path, Skv = 33000 with a ragged last tile).  The forward keeps 64
+    list entries in one register and slides that window along the row: here 2
+    and 4 times."""
+    run_case(80 + D, mask, score, 1, 2, 1, 256, 33000, D, dense=dense, prefix=20000)
+
+
 @pytest.mark.parametrize("score", ["none", "alibi", "bias"])
 def test_dense_without_blockmask(score):
     run_case(31, "none", score, 1, 4, 4, 250, 250, 128, dense=True)
@@ -207,3 +218,65 @@ def test_invalid_arguments_raise():
     with pytest.raises(fa.FAError) as e:
         fa.fa_forward(q, q, q, block_mask=bm)  # built for other lengths
     assert e.value.status == fa.FA_ERR_SHAPE
+
+
+def _diagonal_scores(cap, S):
+    """bf16 Q, K with one attended key per row (the diagonal) whose score is s_q, a
+    dense grid over [-8 cap, 8 cap] plus points near 0: s_q = a_q + b_q with a_q, b_q
+    bf16 (the residual of a_q), both multiplied by K = 1 in dims 0 and 1, so the
+    fp32 product is exact.  Returns q, k bits [1,1,S,64] and s (fp64)."""
+    grid = np.concatenate([np.linspace(-8 * cap, 8 * cap, S - 10),
+                           [0.0, 1e-6, -1e-6, 1e-3, -1e-3, 0.1, -0.1, 1.0, -1.0, 2.5]])
+    a = gen.f32_to_bf16_bits(grid.astype(np.float32))
+    b = gen.f32_to_bf16_bits((grid - fo.bf16_to_f64(a)).astype(np.float32))
+    s = fo.bf16_to_f64(a) + fo.bf16_to_f64(b)
+    q = np.zeros((1, 1, S, 64), dtype=np.uint16)
+    k = np.zeros((1, 1, S, 64), dtype=np.uint16)
+    q[0, 0, :, 0], q[0, 0, :, 1] = a, b
+    k[0, 0, :, 0] = k[0, 0, :, 1] = 0x3F80   # 1.0
+    return q, k, s
+
+
+def _tanh_bound(cap, ref):
+    # a few fp32 roundings of cap * log2(e) * (1 - 2 / (1 + e^(2s/cap))) and of the LSE
+    return cap * 2.0 ** -19 + np.abs(ref) * 2.0 ** -21
+
+
+@pytest.mark.parametrize("cap", [30.0, 50.0, 1.0])
+def test_device_softcap_tanh_error_bound(cap):
+    """The device tanh of the softcap score_mod against fp64 tanh (paper review
+    §2.1 table, softcapping; an approximate tanh is allowed).  With the sliding
+    window 0 every row attends its diagonal key alone, so the forward's LSE is
+    that key's modded score cap * tanh(s / cap); with a one-key cache the same
+    holds for decode."""
+    import torch
+    from block_sparse_attention_fa_amd import fa
+    S = 4096
+    q, k, s = _diagonal_scores(cap, S)
+    ref = cap * np.tanh(s / cap)
+    v = gen.qkv(90, 1, 1, 1, 1, S, 64)[2]
+    qt, kt, vt = (gen.to_torch_bf16(x) for x in (q, k, v))
+    bm = fa.fa_build_block_mask(fa.MaskMod("sliding_causal", window=0), 1, 1, S, S)
+    lse = torch.empty((1, 1, S), dtype=torch.float32, device="cuda")
+    fa.fa_forward(qt, kt, vt, block_mask=bm, score=fa.ScoreMod("softcap", softcap=cap), scale=1.0, lse=lse)
+    torch.cuda.synchronize()
+    got = lse[0, 0].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    print(f"[tanh fwd cap={cap}] max abs {err.max():.3e} at s={s[err.argmax()]:.4g}, "
+          f"max err / bound {(err / _tanh_bound(cap, ref)).max():.3f}", flush=True)
+    assert np.all(err <= _tanh_bound(cap, ref))
+    # decode: sequence b holds one key, q_b . k = s_b
+    qd = q[0, 0][:, None, None, :]                     # [S, 1, 1, 64]
+    kd = np.zeros((S, 1, 128, 64), dtype=np.uint16)
+    kd[:, 0, 0, :] = k[0, 0, 0]
+    lens = torch.ones(S, dtype=torch.int32, device="cuda")
+    bmd = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=lens), S, 1, 1, 128)
+    lsed = torch.empty((S, 1, 1), dtype=torch.float32, device="cuda")
+    fa.fa_decode(gen.to_torch_bf16(qd), gen.to_torch_bf16(kd), gen.to_torch_bf16(kd), block_mask=bmd,
+                 score=fa.ScoreMod("softcap", softcap=cap), scale=1.0, lse=lsed)
+    torch.cuda.synchronize()
+    gd = lsed[:, 0, 0].cpu().numpy().astype(np.float64)
+    errd = np.abs(gd - ref)
+    print(f"[tanh decode cap={cap}] max abs {errd.max():.3e}, max err / bound "
+          f"{(errd / _tanh_bound(cap, ref)).max():.3f}", flush=True)
+    assert np.all(errd <= _tanh_bound(cap, ref))
