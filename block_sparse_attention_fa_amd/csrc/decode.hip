@@ -22,6 +22,8 @@
 // V rows are in flight during pass 2.  Its output is the chunk's normalised
 // partial output and base-2 LSE in a caller-provided fp32 workspace.
 // decode_merge: LSE = log-sum-exp of the chunk LSEs, O = sum_s e^(LSE_s - LSE) O_s.
+#include <mutex>
+
 #include "mods.hpp"
 
 namespace fa {
@@ -419,5 +421,32 @@ fa_status launch_decode(int D, int G, int score_kind, const DecodeParams& P, hip
 }
 
 int decode_max_blocks_per_split() { return kMaxBps; }
+
+// The workspace of fa_decode_noalloc: a device array of the library, one per
+// GPU.  Host code never passes its name to a kernel (on the host the name
+// stands for a host-side shadow, not a device address): the device address is
+// looked up with hipGetSymbolAddress on the first call on each device, with
+// that device current, and kept per device.
+static __device__ __align__(256) float scratch[FA_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+fa_status decode_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FA_OK;
+}
 
 }  // namespace fa

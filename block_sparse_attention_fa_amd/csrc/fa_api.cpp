@@ -262,6 +262,24 @@ fa_status prepare_backward(const fa_attn_args* a, const fa_grad_args* g, BwdPara
   return FA_OK;
 }
 
+fa_status run_decode(const fa_attn_args* a, const FwdParams& p, int mask_kind, const DecodePlan& plan,
+                     void* workspace, hipStream_t stream) {
+  DecodeParams P;
+  P.f = p;
+  P.mask_kind = mask_kind;
+  P.splits = plan.splits;
+  P.blocks_per_split = plan.bps;
+  P.ws_o = (float*)workspace;
+  P.ws_lse = P.ws_o + (size_t)plan.splits * a->B * a->Hq * a->D;
+  P.page_table = a->page_table;
+  P.pt_stride = a->page_table_stride;
+  P.num_pages = a->num_pages;
+  P.q_pos = a->q_pos;
+  const fa_status st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, stream);
+  if (st != FA_OK) return fail(st, "decode launch failed");
+  return FA_OK;
+}
+
 }  // namespace
 
 fa_status launch_backward(int D, int mask_kind, int score_kind, const BwdParams& p, hipStream_t s) {
@@ -386,6 +404,22 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes) {
   return prepare_decode(a, p, mask_kind, plan, *bytes);
 }
 
+fa_status fa_decode_noalloc(const fa_attn_args* a, void* stream) {
+  FwdParams p;
+  int mask_kind;
+  DecodePlan plan;
+  size_t need;
+  fa_status st = prepare_decode(a, p, mask_kind, plan, need);
+  if (st != FA_OK) return st;
+  if (need > (size_t)FA_DECODE_SCRATCH_BYTES)
+    return fail(FA_ERR_WORKSPACE, "decode needs %zu bytes of workspace, above the %u bytes of the library's "
+                                  "scratch (use fa_decode with a workspace)", need, (unsigned)FA_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = decode_scratch(&ws);
+  if (st != FA_OK) return fail(st, "decode scratch address lookup failed");
+  return run_decode(a, p, mask_kind, plan, ws, (hipStream_t)stream);
+}
+
 fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream) {
   FwdParams p;
   int mask_kind;
@@ -397,20 +431,7 @@ fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_byt
   if (workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "decode workspace %zu bytes < %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 3u) != 0) return fail(FA_ERR_WORKSPACE, "decode workspace not 4-byte aligned");
-  DecodeParams P;
-  P.f = p;
-  P.mask_kind = mask_kind;
-  P.splits = plan.splits;
-  P.blocks_per_split = plan.bps;
-  P.ws_o = (float*)workspace;
-  P.ws_lse = P.ws_o + (size_t)plan.splits * a->B * a->Hq * a->D;
-  P.page_table = a->page_table;
-  P.pt_stride = a->page_table_stride;
-  P.num_pages = a->num_pages;
-  P.q_pos = a->q_pos;
-  st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, (hipStream_t)stream);
-  if (st != FA_OK) return fail(st, "decode launch failed");
-  return FA_OK;
+  return run_decode(a, p, mask_kind, plan, workspace, (hipStream_t)stream);
 }
 
 fa_status fa_backward_workspace_size(const fa_attn_args* a, size_t* bytes) {

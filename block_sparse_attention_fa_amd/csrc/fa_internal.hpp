@@ -114,6 +114,8 @@ fa_status launch_forward_document_causal(int D, int score_kind, const FwdParams&
 fa_status launch_forward_prefix_lm(int D, int score_kind, const FwdParams& p, hipStream_t stream);
 fa_status launch_forward_kv_len(int D, int score_kind, const FwdParams& p, hipStream_t stream);
 fa_status launch_decode(int D, int G, int score_kind, const DecodeParams& p, hipStream_t stream);
+// Device address of the current device's decode scratch (FA_DECODE_SCRATCH_BYTES).
+fa_status decode_scratch(void** ptr);
 fa_status launch_backward(int D, int mask_kind, int score_kind, const BwdParams& p, hipStream_t stream);
 fa_status launch_backward_prep(int D, const BwdParams& p, hipStream_t stream);
 fa_status launch_backward_none(int D, int score_kind, const BwdParams& p, hipStream_t stream);

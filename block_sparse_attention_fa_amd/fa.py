@@ -5,7 +5,8 @@ kernels behind the C ABI.  torch supplies device memory and the current
 stream.  The functions keep the C names:
 
     fa_block_mask_dims, fa_build_block_mask, fa_forward,
-    fa_decode_workspace_size, fa_decode
+    fa_decode_workspace_size, fa_decode, fa_decode_noalloc,
+    fa_backward_workspace_size, fa_backward, fa_probe_mfma, fa_probe_copy
 
 plus small helpers to describe mask_mods / score_mods and to inspect a
 BlockMask (ASCII print and sparsity, as on the attention-gym "Concepts"
@@ -82,6 +83,7 @@ SIGNATURES = {
     "fa_forward": (c_int32, [POINTER(AttnArgs), c_void_p]),
     "fa_decode_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
     "fa_decode": (c_int32, [POINTER(AttnArgs), c_void_p, c_size_t, c_void_p]),
+    "fa_decode_noalloc": (c_int32, [POINTER(AttnArgs), c_void_p]),
     "fa_backward_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
     "fa_backward": (c_int32, [POINTER(AttnArgs), POINTER(GradArgs), c_void_p, c_size_t, c_void_p]),
     "fa_probe_mfma": (c_int32, [c_int32, c_int32, c_void_p, POINTER(ctypes.c_double), c_void_p]),
@@ -414,14 +416,7 @@ def fa_decode_workspace_size(q, k, v, block_mask=None, score=None, num_splits=0,
     return n.value
 
 
-def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
-              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None, page_table=None,
-              q_pos=None):
-    """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D], or, with an int32
-    page_table [B, blocks], against page pools [num_pages, Hkv, 128, D] where
-    logical block j of sequence b is page page_table[b, j].  q_pos (int32 [B],
-    optional) is each query token's position, the q index the score_mods see
-    (0 when not given); pass kv_len - 1 for the newest token of a causal cache."""
+def _decode_args(q, k_cache, v_cache, block_mask, score, scale, num_splits, out, lse, stream, page_table, q_pos):
     import torch
     if q_pos is not None:
         _need(q_pos.dtype == torch.int32 and q_pos.dim() == 1 and q_pos.stride(0) == 1,
@@ -434,6 +429,20 @@ def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: S
             out = torch.empty_like(q)
     a = _attn_args(q, k_cache, v_cache, out, lse, block_mask, score, scale, num_splits, page_table)
     a.q_pos = q_pos.data_ptr() if q_pos is not None else None
+    return a, out
+
+
+def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
+              scale=0.0, num_splits=0, out=None, lse=None, workspace=None, stream=None, page_table=None,
+              q_pos=None):
+    """Split-KV decode: q [B,Hq,1,D] against caches [B,Hkv,KV,D], or, with an int32
+    page_table [B, blocks], against page pools [num_pages, Hkv, 128, D] where
+    logical block j of sequence b is page page_table[b, j].  q_pos (int32 [B],
+    optional) is each query token's position, the q index the score_mods see
+    (0 when not given); pass kv_len - 1 for the newest token of a causal cache."""
+    import torch
+    a, out = _decode_args(q, k_cache, v_cache, block_mask, score, scale, num_splits, out, lse, stream,
+                          page_table, q_pos)
     n = c_size_t()
     _check(lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     if workspace is None:
@@ -441,6 +450,17 @@ def fa_decode(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: S
             workspace = torch.empty(max(1, n.value // 4), dtype=torch.float32, device=q.device)
     _check(lib().fa_decode(ctypes.byref(a), c_void_p(workspace.data_ptr()),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, block_mask: BlockMask | None = None, score: ScoreMod | None = None,
+                      scale=0.0, num_splits=0, out=None, lse=None, stream=None, page_table=None, q_pos=None):
+    """fa_decode with the library's own scratch instead of a workspace: the C call
+    allocates nothing (pass `out` to keep this wrapper from allocating either).
+    Calls on one GPU share the scratch and must not overlap."""
+    a, out = _decode_args(q, k_cache, v_cache, block_mask, score, scale, num_splits, out, lse, stream,
+                          page_table, q_pos)
+    _check(lib().fa_decode_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

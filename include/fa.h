@@ -23,8 +23,10 @@
  *    returns a message naming the failed check (per calling thread).
  *  - Launch failures return FA_ERR_HIP.  Faults inside a kernel surface at
  *    the caller's next synchronisation, as for any HIP kernel.
- *  - No global mutable state (the last-error message is per thread): calls
- *    may be made from several threads at once.
+ *  - The only global state is the last-error message (per thread) and, for
+ *    fa_decode_noalloc, a per-device pointer set once under a lock: calls may be
+ *    made from several threads at once (fa_decode_noalloc calls on one GPU
+ *    share its scratch and must not overlap).
  *  - Changing any runtime parameter (window, prefix length, document ids,
  *    lengths, slopes, cap, bias tensor, BlockMask contents) never needs a
  *    rebuild: only the mask/score *kind* selects compiled code (Concepts,
@@ -249,6 +251,25 @@ fa_status fa_decode_workspace_size(const fa_attn_args* a, size_t* bytes);
  * page_table_stride < ceil(Skv / FA_BLOCK), FA_ERR_UNSUPPORTED for a mask kind
  * other than NONE / KV_LEN, and FA_ERR_WORKSPACE. */
 fa_status fa_decode(const fa_attn_args* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch size of fa_decode_noalloc: decode calls whose workspace
+ * (fa_decode_workspace_size) exceeds this are rejected by it. */
+#define FA_DECODE_SCRATCH_BYTES (32u << 20)
+
+/* fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory around the call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, kernels and result
+ * as fa_decode; the split partial outputs and LSEs go to a device array
+ * inside the library (FA_DECODE_SCRATCH_BYTES per GPU, held by every GPU the
+ * library runs on until the process ends; its address is looked up on the first
+ * call on each device).  Nothing is allocated or freed by the call.  Every call
+ * on one GPU shares that array, so calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and must be ordered by the
+ * caller; the array needs no clearing between calls (every split writes its
+ * whole row before the merge reads it).
+ * Errors: as fa_decode, with FA_ERR_WORKSPACE when the workspace fa_decode
+ * would need exceeds FA_DECODE_SCRATCH_BYTES (checked before any HIP call). */
+fa_status fa_decode_noalloc(const fa_attn_args* a, void* stream);
 
 /* Host only.  Bytes of workspace fa_backward needs: two fp32 values (base-2
  * LSE and Delta = rowsum(dO * O)) per query row, rows padded to whole tiles.

@@ -350,3 +350,16 @@ def test_probe_validation_codes():
     assert L.fa_probe_copy(0x10000, 0x20000, 0, None) == fa.FA_ERR_SHAPE
     assert L.fa_probe_copy(0x10000, 0x20000, 24, None) == fa.FA_ERR_SHAPE
     assert L.fa_probe_copy(0x10008, 0x20000, 32, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_size_limit_is_checked_on_the_host():
+    """fa_decode_noalloc rejects a decode whose workspace would exceed the library's
+    scratch (FA_DECODE_SCRATCH_BYTES = 32 MiB) before any HIP call."""
+    a = _args(B=64, Hq=64, Hkv=8, Sq=1, Skv=32768, D=128)
+    n = ctypes.c_size_t()
+    assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
+    assert n.value > (32 << 20)
+    assert fa.lib().fa_decode_noalloc(ctypes.byref(a), None) == fa.FA_ERR_WORKSPACE
+    assert "scratch" in fa.lib().fa_last_error().decode()
+    a = _args(Sq=2)
+    assert fa.lib().fa_decode_noalloc(ctypes.byref(a), None) == fa.FA_ERR_SHAPE
