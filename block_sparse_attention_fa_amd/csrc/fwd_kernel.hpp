@@ -308,6 +308,7 @@ void fwd_kernel(FwdParams p) {
   // then only raised when a score exceeds it by more than kRescaleSlack.  Scores
   // are produced relative to it (y = x2 - m_run), so exp2(y) needs no subtraction.
   float m_run = -INFINITY;
+  if constexpr (Score::kBounded) m_run = Score::bound(srow);  // fixed reference: no running max
   // This lane's half of the row sum, in four fp32 partial sums of the
   // exponentials (plain adds: on gfx950 a v_dot2 instruction cannot run while
   // an MFMA is in flight, a v_add can).
@@ -340,9 +341,11 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vaddr[dt] = lds_address(vl) + 2 * voff[dt];
   };
-  // MFMA i (0..2*KS-1) of S^T = K Q^T for a 64-key sub-tile: (32-key block i / KS, k-step i % KS)
+  // MFMA i (0..2*KS-1) of S^T = K Q^T for a 64-key sub-tile: (32-key block i % 2, k-step i / 2).
+  // The two key blocks alternate, so consecutive MFMAs accumulate into different
+  // registers: two independent chains instead of one 8-long chain per block.
   auto qk_mfma = [&](f32x16_t (&acc)[2], int i) {
-    const int mt = i / KS, s = i % KS;
+    const int mt = i & 1, s = i >> 1;
     const bf16x8_t a = ((const lds_bf16x8_t*)(uintptr_t)kaddr[s])[mt * 32 * D / 8];
     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? acc0 : acc[mt], 0, 0, 0);
   };
@@ -449,13 +452,13 @@ void fwd_kernel(FwdParams p) {
           y = Score::apply(st, s_cur[mt][r], Score::kReadsMemory ? min(cr, lim - 1) : cr);
         }
         s_cur[mt][r] = y;
-        ymax = fmaxf(ymax, y);
+        if constexpr (!Score::kBounded) ymax = fmaxf(ymax, y);
         if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
       }
       // Keep the row max of the unmasked scores here, beside the PV MFMAs: left
       // alone, the compiler moves it (and a copy of every score register) past
       // the masked-pass branch, where no MFMA is in flight to cover it.
-      asm volatile("" : "+v"(ymax));
+      if constexpr (!Score::kBounded) asm volatile("" : "+v"(ymax));
       if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
         const auto mtl = Mask::tile(mrow, kvb);
         ymax = -INFINITY;
@@ -482,16 +485,16 @@ void fwd_kernel(FwdParams p) {
           }
           const float y = keep ? s_cur[mt][r] : -INFINITY;
           s_cur[mt][r] = y;
-          ymax = fmaxf(ymax, y);
+          if constexpr (!Score::kBounded) ymax = fmaxf(ymax, y);
         }
       }
 #pragma unroll
       for (int i = 16; i < 4 * DT; ++i) pv_mfma(p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
 
-      // ---- C: raise the reference max when needed
-      ymax = max_across_halves(ymax);
-      const bool raise = ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY);
-      if (__any(raise)) {
+      // ---- C: raise the reference max when needed (never for a bounded score)
+      if constexpr (!Score::kBounded) ymax = max_across_halves(ymax);
+      const bool raise = !Score::kBounded && (ymax > kRescaleSlack || (m_run == -INFINITY && ymax > -INFINITY));
+      if (!Score::kBounded && __any(raise)) {
         const float m_new = fmaxf(m_run, m_ref + ymax);
         const float shift = m_new == -INFINITY ? 0.0f : m_ref - m_new;
         const float alpha = m_run == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -570,6 +573,13 @@ struct LaunchFwd {
   void operator()() {
     const int NQ = (p.Sq + kBM - 1) / kBM;
     const long long total = (long long)NQ * p.Hq * p.B;
+    if constexpr (std::is_same<Score, ScoreSoftcap>::value) {
+      if (p.score.cap_log2 <= kBoundedMaxLog2) {
+        hipLaunchKernelGGL((fwd_kernel<D, Mask, ScoreSoftcapBounded>), dim3((unsigned)total), dim3(kFwdThreads), 0,
+                           stream, p);
+        return;
+      }
+    }
     if constexpr (std::is_same<Score, ScoreBias>::value) {
       const ScoreParams& s = p.score;
       const bool aligned = ((uintptr_t)s.bias % 16 == 0) && s.bs0 % 8 == 0 && s.bs1 % 8 == 0 &&

@@ -306,6 +306,7 @@ struct ScoreNone {
   static constexpr bool kReadsMemory = false;
   static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
+  static constexpr bool kBounded = false;
   struct Row {
     float c;
   };
@@ -330,6 +331,7 @@ struct ScoreAlibi {
   static constexpr bool kReadsMemory = false;
   static constexpr bool kPreload = true;
   static constexpr bool kStagesBias = false;
+  static constexpr bool kBounded = false;
   struct Row {
     float c;    // scale * log2e
     float sl;   // slope[h] * log2e
@@ -377,6 +379,7 @@ struct ScoreSoftcap {
   static constexpr bool kReadsMemory = false;
   static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
+  static constexpr bool kBounded = false;
   struct Row {
     float k;     // 2 * scale / cap * log2e
     float c2;    // cap * log2e
@@ -415,6 +418,7 @@ struct ScoreRelPos {
   static constexpr bool kReadsMemory = false;
   static constexpr bool kPreload = true;
   static constexpr bool kStagesBias = false;
+  static constexpr bool kBounded = false;
   struct Row {
     float c;
     int q;
@@ -455,6 +459,7 @@ struct ScoreBias {
   static constexpr bool kReadsMemory = true;
   static constexpr bool kPreload = false;
   static constexpr bool kStagesBias = false;
+  static constexpr bool kBounded = false;
   struct Row {
     float c;
     const uint16_t* row;  // bias[b, h, q, :]
@@ -505,6 +510,30 @@ struct ScoreBiasTiled : ScoreBias {
     return fmaf(s, t.c, fmaf(kLog2e, bf16_bits_to_float(b), t.add));
   }
 };
+
+// Softcapping with the softmax reference fixed at the cap: |cap tanh(x)| <= cap,
+// so with the reference max at cap * log2(e) every exponent lies in
+// [-2 cap log2(e), 0] and no running max is needed (softmax is unchanged by the
+// shift).  Chosen by the launch when cap log2(e) <= kBoundedMaxLog2: every
+// weight is then >= 2^-112, normal in fp32 and bf16, and so are its products
+// with any V element of magnitude >= 2^-14.
+//
+// Relative to the bound, the score is y = cap log2(e) (tanh(x) - 1) =
+// -2 cap log2(e) / (1 + e^{2x}), computed as 1 / (a (1 + e^{2x})) with
+// a = -1 / (2 cap log2(e)): one multiply-add and a reciprocal after the exp2.
+struct ScoreSoftcapBounded : ScoreSoftcap {
+  static constexpr bool kBounded = true;
+  static __device__ __forceinline__ float bound(const Row& r) { return r.c2; }
+  struct Tile {
+    float k, a;
+  };
+  static __device__ __forceinline__ Tile tile(const Row& r, int, float) { return {r.k, -0.5f / r.c2}; }
+  static __device__ __forceinline__ float apply(const Tile& t, float s, int) {
+    const float e = __builtin_amdgcn_exp2f(s * t.k);
+    return __builtin_amdgcn_rcpf(fmaf(e, t.a, t.a));
+  }
+};
+constexpr float kBoundedMaxLog2 = 56.0f;
 
 template <class F>
 __host__ __device__ inline bool dispatch_score(int kind, F&& f) {

@@ -101,12 +101,17 @@ _lib = None
 
 
 def lib():
-    """The loaded libfa.so.  Raises if it has not been built: there is no fallback path."""
+    """The loaded libfa.so.  Raises if it has not been built: there is no fallback path.
+
+    torch is imported first: its HIP runtime must be the one libfa.so binds to
+    (loaded the other way round, the process would hold two HIP runtimes and
+    the library's launches would not see torch's streams)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m block_sparse_attention_fa_amd._build`")
+        import torch  # noqa: F401  (see above)
         l = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(l, name)
