@@ -59,6 +59,7 @@ MaskParams mask_params(const fa_mask_desc& m) {
   p.doc = m.doc_ids;
   p.doc_stride_b = m.doc_stride_b;
   p.kv_len = m.kv_len;
+  p.doc_vec = m.doc_ids != nullptr && aligned16(m.doc_ids) && m.doc_stride_b % 4 == 0;
   return p;
 }
 

@@ -16,6 +16,7 @@ struct MaskParams {
   const int* doc;
   long long doc_stride_b;
   const int* kv_len;
+  int doc_vec;  // doc (and every batch row of it) 16-byte aligned: ids can be read 4 at a time
 };
 
 // Runtime parameters of the score_mods, with host-folded constants.

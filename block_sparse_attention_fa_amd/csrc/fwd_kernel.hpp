@@ -154,6 +154,12 @@ void fwd_kernel(FwdParams p) {
   // staged bias): row r holds its 8 16-byte chunks c at slot c ^ (r % 8).
   constexpr bool BL = Score::kStagesBias;
   __shared__ __align__(16) uint16_t b_lds[BL ? 2 : 1][BL ? kBM * HB : 8];
+  // Document ids of sub-tiles j, j+1, j+2 (masks that read them, D = 64, where
+  // the 768 bytes fit beside two workgroups' rings): the masked pass then reads
+  // them from LDS instead of issuing global loads, whose wait would also wait
+  // for the tile loads in flight.
+  constexpr bool DL = Mask::kReadsMemory && D == 64;
+  __shared__ __align__(16) int doc_lds[DL ? 3 : 1][DL ? HB : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -243,7 +249,20 @@ void fwd_kernel(FwdParams p) {
     }
   };
   auto kv0_of = [&](int j) { return kb_of(j / SPT) * kBN + HB * (j % SPT); };
-  auto issue_k = [&](int j) { issue_one(Kp, ksb, k_lds[j % NK], kchunk, k_voff, kv0_of(j)); };
+  // Document ids of sub-tile j -> doc_lds[j % 3]: 16 lanes of wave 0, 16 bytes
+  // each, when the ids are 16-byte aligned and the sub-tile is whole (else the
+  // masked pass reads them from global memory).
+  const int* doc_row = nullptr;
+  if constexpr (DL) doc_row = p.mask.doc + (long long)b * p.mask.doc_stride_b;
+  auto issue_k = [&](int j) {
+    issue_one(Kp, ksb, k_lds[j % NK], kchunk, k_voff, kv0_of(j));
+    if constexpr (DL) {
+      const int kv0 = kv0_of(j);
+      if (p.mask.doc_vec && wave == 0 && kv0 + HB <= p.Skv) {
+        if (lane < HB / 4) dma16(doc_row + kv0 + 4 * lane, lds_address(doc_lds[j % 3]));
+      }
+    }
+  };
   auto issue_v = [&](int j) { issue_one(Vp, vsb, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
   // Bias tile of sub-tile j -> b_lds[j % 2]: wave w issues slots 64 (4i + w) + lane
   // (i < 4), i.e. row 32 i + 8 w + lane / 8, stored slot lane % 8 holding chunk
@@ -465,12 +484,29 @@ void fwd_kernel(FwdParams p) {
         // A mask that reads memory (document ids) is evaluated for every element
         // first, in-bounds and without branches, so all its loads are in flight
         // at once; the others are evaluated where needed.
+        // Document ids come in runs of 4 keys (16 bytes) per lane: one vector
+        // load each when the ids are 16-byte aligned and the tile is whole.
         bool mk[32];
         if constexpr (Mask::kReadsMemory) {
+          if (DL && p.mask.doc_vec && !ragged) {
+            typedef int i32x4_t __attribute__((ext_vector_type(4)));
+            const uint32_t ids0 = lds_address(doc_lds[DL ? j % 3 : 0]) + 16 * hh;  // keys kvb = kvt0 + 4 hh
 #pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            const int mt = e >> 4, r = e & 15;
-            mk[e] = Mask::keep(mtl, min(32 * mt + 8 * (r >> 2) + (r & 3), lim - 1));
+            for (int g = 0; g < 8; ++g) {  // keys kvb + 32 (g / 4) + 8 (g % 4) + {0..3}
+              const int cr = 32 * (g >> 2) + 8 * (g & 3);
+              const i32x4_t v = *(const __attribute__((address_space(3))) i32x4_t*)(uintptr_t)(ids0 + 4 * cr);
+              const int ids[4] = {v[0], v[1], v[2], v[3]};
+              bool k4[4];
+              Mask::keep4(mtl, cr, ids, k4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mk[4 * g + i] = k4[i];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+              const int mt = e >> 4, r = e & 15;
+              mk[e] = Mask::keep(mtl, min(32 * mt + 8 * (r >> 2) + (r & 3), lim - 1));
+            }
           }
         }
 #pragma unroll

@@ -78,6 +78,9 @@ struct MaskNone {
   struct Tile {};
   static __device__ __forceinline__ Tile tile(const Row&, int) { return {}; }
   static __device__ __forceinline__ bool keep(const Tile&, int) { return true; }
+  static __device__ __forceinline__ void keep4(const Tile&, int, const int (&)[4], bool (&k)[4]) {
+    k[0] = k[1] = k[2] = k[3] = true;
+  }
   static __device__ __forceinline__ int classify(const MaskParams&, int, int, int, int, int, int, int) {
     return kTileFull;
   }
@@ -97,6 +100,10 @@ struct MaskCausal {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.q - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr <= t.dq; }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&)[4], bool (&k)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = keep(t, cr + i);
+  }
   static __device__ __forceinline__ int classify(const MaskParams&, int, int, int q0, int q1, int k0, int k1, int) {
     return classify_threshold((long long)q0 - k1, (long long)q1 - k0);  // x = q - kv
   }
@@ -118,6 +125,10 @@ struct MaskWindow {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.lo - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr >= t.lo; }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&)[4], bool (&k)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = keep(t, cr + i);
+  }
   static __device__ __forceinline__ int classify(const MaskParams& p, int, int, int q0, int q1, int k0, int k1, int) {
     return classify_threshold((long long)k0 - q1 + p.window, (long long)k1 - q0 + p.window);  // x = kv - q + window
   }
@@ -142,6 +153,12 @@ struct MaskDocument {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.doc + kvb, r.dq}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return t.doc[cr] == t.dq; }
+  // Keys cr..cr+3 given their document ids (read by the caller, e.g. from a
+  // copy of the tile's ids in LDS).
+  static __device__ __forceinline__ void keep4(const Tile& t, int, const int (&ids)[4], bool (&k)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = ids[i] == t.dq;
+  }
   // One document on each side decides the tile; so do disjoint id ranges.
   static __device__ int classify(const MaskParams& p, int b, int, int q0, int q1, int k0, int k1, int lane) {
     const int* d = p.doc + (long long)b * p.doc_stride_b;
@@ -178,6 +195,10 @@ struct MaskPrefix {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&)[4], bool (&k)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = keep(t, cr + i);
+  }
   static __device__ __forceinline__ int classify(const MaskParams& p, int, int, int, int, int k0, int k1, int) {
     return classify_threshold((long long)p.prefix_len - 1 - k1, (long long)p.prefix_len - 1 - k0);
   }
@@ -197,6 +218,10 @@ struct MaskKvLen {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {r.n - kvb}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return cr < t.n; }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&)[4], bool (&k)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = keep(t, cr + i);
+  }
   static __device__ __forceinline__ int classify(const MaskParams& p, int b, int, int, int, int k0, int k1, int) {
     const int n = p.kv_len[b];
     return classify_threshold((long long)n - 1 - k1, (long long)n - 1 - k0);
@@ -222,6 +247,13 @@ struct MaskAnd {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) && B::keep(t.b, cr); }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&ids)[4], bool (&k)[4]) {
+    bool ka[4], kb[4];
+    A::keep4(t.a, cr, ids, ka);
+    B::keep4(t.b, cr, ids, kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = ka[i] && kb[i];
+  }
   static __device__ int classify(const MaskParams& p, int b, int h, int q0, int q1, int k0, int k1, int lane) {
     const int ca = A::classify(p, b, h, q0, q1, k0, k1, lane);
     if (ca == kTileEmpty) return kTileEmpty;
@@ -251,6 +283,13 @@ struct MaskOr {
   };
   static __device__ __forceinline__ Tile tile(const Row& r, int kvb) { return {A::tile(r.a, kvb), B::tile(r.b, kvb)}; }
   static __device__ __forceinline__ bool keep(const Tile& t, int cr) { return A::keep(t.a, cr) || B::keep(t.b, cr); }
+  static __device__ __forceinline__ void keep4(const Tile& t, int cr, const int (&ids)[4], bool (&k)[4]) {
+    bool ka[4], kb[4];
+    A::keep4(t.a, cr, ids, ka);
+    B::keep4(t.b, cr, ids, kb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k[i] = ka[i] || kb[i];
+  }
   static __device__ int classify(const MaskParams& p, int b, int h, int q0, int q1, int k0, int k1, int lane) {
     const int ca = A::classify(p, b, h, q0, q1, k0, k1, lane);
     if (ca == kTileFull) return kTileFull;
