@@ -137,12 +137,51 @@ def cpu_baseline(q, k, v, seconds):
             "cpu_model": model, "cpu_count": os.cpu_count(), "blas": blas}
 
 
-class Timer:
-    """HIP events recorded on the launch stream around a batch of calls."""
+def sample_power(fn, seconds=4.0):
+    """Run fn back to back for `seconds` while `amd-smi metric -p -c` samples the
+    board power and the graphics clocks (three samples, from the second second on).
+    Returns {"socket_power_w": [...], "gfx_clk_mhz": [...]} or an error note."""
+    import subprocess
+    import threading
+    import torch
+    out = {"socket_power_w": [], "gfx_clk_mhz": []}
 
-    def __init__(self, stream):
+    def sampler():
+        time.sleep(1.0)
+        for _ in range(3):
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                out["socket_power_w"].append(g["power"]["socket_power"]["value"])
+                clk = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+                out["gfx_clk_mhz"].append(round(sum(clk) / len(clk)))
+            except Exception as e:  # no amd-smi, or another JSON layout
+                out["error"] = f"{type(e).__name__}: {e}"
+                return
+            time.sleep(0.5)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    th.join()
+    return out
+
+
+class Timer:
+    """HIP events recorded on the launch stream around a batch of calls; with
+    power=True each measurement is followed by sample_power on the same call."""
+
+    def __init__(self, stream, power=False):
         import torch
         self.stream = stream
+        self.power = power
+        self.last_power = None
         self.e0 = torch.cuda.Event(enable_timing=True)
         self.e1 = torch.cuda.Event(enable_timing=True)
 
@@ -156,6 +195,8 @@ class Timer:
             fn()
         self.e1.record(self.stream)
         torch.cuda.synchronize()
+        if self.power:
+            self.last_power = sample_power(fn)
         return self.e0.elapsed_time(self.e1) / calls
 
 
@@ -170,15 +211,33 @@ def leg_peaks(T, dev):
         flops["n"] = fa.fa_probe_mfma(wgs, iters, sink)
 
     mfma_ms = min(T.ms(mfma, 20, 30 if i == 0 else 2) for i in range(3))
+    mfma_power = T.last_power
+
+    def mfma_random():
+        flops["r"] = fa.fa_probe_mfma(wgs, iters, sink, random_operands=True)
+
+    rand_ms = min(T.ms(mfma_random, 20, 10 if i == 0 else 2) for i in range(3))
+    rand_power = T.last_power
     n = 1 << 30
     src = torch.zeros(n // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     copy_ms = min(T.ms(lambda: fa.fa_probe_copy(src, dst), 20, 10 if i == 0 else 2) for i in range(3))
-    del src, dst, sink
-    return {"mfma_bf16_tflops": round(flops["n"] / (mfma_ms * 1e-3) / 1e12, 1),
-            "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 v_mfma_f32_32x32x16_bf16, best of 3 x 20 launches",
+    copy_power = T.last_power
+    del src, dst
+    rsink = torch.empty(8192, dtype=torch.int32, device=dev)
+    rsrc = torch.zeros(n, dtype=torch.bfloat16, device=dev)   # 2 GiB read per launch
+    read_ms = min(T.ms(lambda: fa.fa_probe_read(rsrc, rsink), 20, 10 if i == 0 else 2) for i in range(3))
+    del sink, rsrc, rsink
+    return {"power": {"mfma_probe": mfma_power, "mfma_probe_random": rand_power, "copy_probe": copy_power,
+                      "read_probe": T.last_power} if T.power else None,
+            "mfma_bf16_tflops": round(flops["n"] / (mfma_ms * 1e-3) / 1e12, 1),
+            "mfma_bf16_random_operands_tflops": round(flops["r"] / (rand_ms * 1e-3) / 1e12, 1),
+            "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 v_mfma_f32_32x32x16_bf16, best of 3 x 20 "
+                          "launches; constant operands, and random bf16 operands alternating between two sets",
             "copy_gbs": round(2.0 * n / (copy_ms * 1e-3) / 1e9, 1),
             "copy_probe": "1 GiB read + 1 GiB written per launch, 16-byte non-temporal loads/stores, best of 3 x 20",
+            "read_gbs": round(2.0 * n / (read_ms * 1e-3) / 1e9, 1),
+            "read_probe": "2 GiB read per launch, 16-byte non-temporal loads, best of 3 x 20",
             "published": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
 
 
@@ -221,7 +280,8 @@ def leg_sliding(T, dev, peaks):
     tf = flops / (ms * 1e-3) / 1e12
     n_part, n_full = int((cls == 1).sum()), int((cls == 2).sum())
     return {"workload": c["name"], "kernel_ms": round(ms, 4), "attended_tflops": round(tf, 2),
-            "attended_flops": flops, "tiles_partial": n_part, "tiles_full": n_full,
+            "attended_flops": flops, "power": T.last_power if T.power else None,
+            "tiles_partial": n_part, "tiles_full": n_full,
             "executed_tile_tflops": round(4.0 * D * 128 * 128 * (n_part + n_full) * B * H / (ms * 1e-3) / 1e12, 2),
             "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", peaks.get("mfma_bf16_tflops"),
                                  read_traffic("fwd_sliding_softcap_16384_traffic.md", SLIDE_SOURCES),
@@ -261,12 +321,13 @@ def leg_document(T, dev, peaks):
     del bias
     torch.cuda.empty_cache()
     return {"workload": c["name"], "kernel_ms": round(ms, 4), "documents": int(lens.size),
+            "power": T.last_power if T.power else None,
             "attended_tflops": round(4.0 * D * n_att / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(4.0 * D * n_att / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "tiles_partial": n_part, "tiles_full": n_full, "algorithmic_bytes": alg,
             "block_granular_bytes": qkvo + tile_bias,
             "block_granular_gbs": round((qkvo + tile_bias) / (ms * 1e-3) / 1e9, 1),
-            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", peaks.get("copy_gbs"),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", peaks.get("read_gbs"),
                                  read_traffic("fwd_document_bias_16384_traffic.md", DOC_SOURCES),
                                  kernel="fwd_kernel<64, MaskDocumentCausal, ScoreBiasTiled>",
                                  bytes_definition="Q, K, V read and O written once + the bf16 bias at attended positions")}
@@ -297,9 +358,10 @@ def leg_decode(T, dev, peaks, stream):
     dec_bytes = kv_bytes + 2 * Bd * Hq * Dd * 2
     gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     res = {"workload": DEC["name"], "ms": round(dec_ms, 4), "GB/s": round(gbs, 1),
+           "power": T.last_power if T.power else None,
            "untimed_calls": settle, "timed_calls": calls, "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
            "algorithmic_bytes": dec_bytes,
-           "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", peaks.get("copy_gbs"),
+           "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", peaks.get("read_gbs"),
                                 read_traffic("decode_gqa4_kv32768_traffic.md", DEC_SOURCES),
                                 kernels="decode_partial_kernel<128,4,ScoreSoftcap,false> + decode_merge_kernel<128>")}
     # The same caches as a compact page pool (paper review §4.5): only the
@@ -354,6 +416,7 @@ def leg_backward(T, dev, qt, kt, vt):
     n_att = B * H * S * (S + 1) // 2
     tf = 10.0 * D * n_att / (ms * 1e-3) / 1e12
     return {"workload": "backward of " + FWD["name"], "ms": round(ms, 4), "attended_tflops": round(tf, 2),
+            "power": T.last_power if T.power else None,
             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_attended_position": "10*D (S, dP, dV, dK, dQ products)",
             "kernels": "bwd_prep + bwd_dq_kernel + bwd_dkdv_kernel", "untimed_calls": settle, "timed_calls": calls}
@@ -431,6 +494,9 @@ def main():
                     help="comma-separated subset of " + ",".join(LEGS) + " (the timed step is 'main')")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power", action="store_true",
+                    help="after each leg's timing, loop its workload for 4 s and sample board power and "
+                         "graphics clocks with amd-smi (reported under 'power')")
     ap.add_argument("--ablation", action="store_true",
                     help="only time the block-skipping ablation and the sliding-window sparsity sweep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -469,7 +535,7 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
-    T = Timer(stream)
+    T = Timer(stream, power=args.power)
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -533,6 +599,7 @@ def main():
         t1 = time.perf_counter()
         step_ms = (t1 - t0) * 1e3 / args.steps
         fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        main_power = sample_power(step) if args.power else None
         build_ms = T.ms(lambda: fa._check(L.fa_build_block_mask(ctypes.byref(bm.c), S, S, sptr)), 10, 0)
         cls = bm.classes()
         n_part, n_full = int((cls == 1).sum()), int((cls == 2).sum())
@@ -550,7 +617,7 @@ def main():
             "config": {"workload": FWD["name"], "B": B, "H": H, "S": S, "D": D, "mask": "causal",
                        "score_mod": "alibi", "block": 128, "step": "fa_build_block_mask + fa_forward",
                        "legs_before_timed_step": [x for x in legs if x != "main"]},
-            "fwd": {"kernel_ms": round(fwd_ms, 4), "attended_tflops": round(fwd_tflops, 2),
+            "fwd": {"kernel_ms": round(fwd_ms, 4), "attended_tflops": round(fwd_tflops, 2), "power": main_power,
                     "frac_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                     "executed_tile_tflops": round(exec_flops / (fwd_ms * 1e-3) / 1e12, 2),
                     "tiles_partial": n_part, "tiles_full": n_full, "blockmask_build_ms": round(build_ms, 4),

@@ -35,6 +35,7 @@ constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kMaxBps = 8;  // kv tiles per split at most
 constexpr int kMaxRows = kMaxBps * FA_BLOCK;
+constexpr int kScPad = 16;
 
 struct EvalMask {
   const MaskParams& mp;
@@ -77,7 +78,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPR, rr = lane / LPR;
 
-  __shared__ float sc[G][kMaxRows];
+  // scores of the chunk's rows per query head; the rows of the G heads are
+  // kScPad floats apart beyond a multiple of 64 banks, so the G lanes of a key
+  // row that store its G scores hit different banks
+  __shared__ float sc[G][kMaxRows + kScPad];
   __shared__ float red[kDecWaves][G];
   __shared__ float osum[kDecWaves][G][D];
 

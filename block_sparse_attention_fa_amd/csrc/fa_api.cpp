@@ -9,6 +9,10 @@
 #include "fa_internal.hpp"
 
 namespace fa {
+// Measurement probes (probe.hip).
+int probe_read_workgroups(size_t bytes);
+fa_status launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -463,12 +467,23 @@ fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* worksp
   return FA_OK;
 }
 
-fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, float* sink, double* flops, void* stream) {
+fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, int32_t random_operands, float* sink, double* flops,
+                        void* stream) {
   if (sink == nullptr || flops == nullptr) return fail(FA_ERR_NULL, "sink and flops must be non-NULL");
   if (workgroups < 1 || iterations < 1) return fail(FA_ERR_SHAPE, "workgroups and iterations must be >= 1");
   *flops = probe_mfma_flops(workgroups, iterations);
-  const fa_status st = launch_probe_mfma(workgroups, iterations, sink, (hipStream_t)stream);
+  const fa_status st = launch_probe_mfma(workgroups, iterations, random_operands != 0, sink, (hipStream_t)stream);
   return st == FA_OK ? FA_OK : fail(st, "MFMA probe launch failed");
+}
+
+fa_status fa_probe_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  if (src == nullptr || sink == nullptr) return fail(FA_ERR_NULL, "src and sink must be non-NULL");
+  if (bytes == 0 || bytes % 16 != 0) return fail(FA_ERR_SHAPE, "bytes must be a positive multiple of 16");
+  if (!aligned16(src)) return fail(FA_ERR_UNSUPPORTED, "src must be 16-byte aligned");
+  if (sink_words < (size_t)probe_read_workgroups(bytes))
+    return fail(FA_ERR_SHAPE, "sink holds %zu words, the probe writes %d", sink_words, probe_read_workgroups(bytes));
+  const fa_status st = launch_probe_read(src, bytes, sink, (hipStream_t)stream);
+  return st == FA_OK ? FA_OK : fail(st, "read probe launch failed");
 }
 
 fa_status fa_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {

@@ -101,7 +101,7 @@ struct BuildParams {
 };
 
 fa_status launch_block_mask(int mask_kind, const BuildParams& p, hipStream_t stream);
-fa_status launch_probe_mfma(int workgroups, int iterations, float* sink, hipStream_t stream);
+fa_status launch_probe_mfma(int workgroups, int iterations, int random_operands, float* sink, hipStream_t stream);
 double probe_mfma_flops(int workgroups, int iterations);
 fa_status launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 fa_status launch_forward(int D, int mask_kind, int score_kind, const FwdParams& p, hipStream_t stream);

@@ -86,8 +86,9 @@ SIGNATURES = {
     "fa_decode_noalloc": (c_int32, [POINTER(AttnArgs), c_void_p]),
     "fa_backward_workspace_size": (c_int32, [POINTER(AttnArgs), POINTER(c_size_t)]),
     "fa_backward": (c_int32, [POINTER(AttnArgs), POINTER(GradArgs), c_void_p, c_size_t, c_void_p]),
-    "fa_probe_mfma": (c_int32, [c_int32, c_int32, c_void_p, POINTER(ctypes.c_double), c_void_p]),
+    "fa_probe_mfma": (c_int32, [c_int32, c_int32, c_int32, c_void_p, POINTER(ctypes.c_double), c_void_p]),
     "fa_probe_copy": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
+    "fa_probe_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
 }
 
 
@@ -514,15 +515,15 @@ def fa_backward(q, k, v, out, lse, dout, block_mask: BlockMask | None = None, sc
 
 # --- measurement probes ------------------------------------------------------------
 
-def fa_probe_mfma(workgroups, iterations, sink, stream=None):
+def fa_probe_mfma(workgroups, iterations, sink, random_operands=False, stream=None):
     """Launch the bf16 MFMA loop (include/fa.h); returns its flop count.
     sink: float32 GPU tensor of >= workgroups * 256 elements."""
     import torch
     _need(sink.dtype == torch.float32 and sink.is_cuda and sink.numel() >= workgroups * 256,
           "sink must be a float32 GPU tensor of >= workgroups * 256 elements")
     flops = ctypes.c_double()
-    _check(lib().fa_probe_mfma(int(workgroups), int(iterations), c_void_p(sink.data_ptr()), ctypes.byref(flops),
-                               _stream(stream)))
+    _check(lib().fa_probe_mfma(int(workgroups), int(iterations), 1 if random_operands else 0,
+                               c_void_p(sink.data_ptr()), ctypes.byref(flops), _stream(stream)))
     return flops.value
 
 
@@ -532,3 +533,12 @@ def fa_probe_copy(src, dst, stream=None):
     _need(src.is_cuda and dst.is_cuda and dst.numel() * dst.element_size() == n and src.is_contiguous()
           and dst.is_contiguous(), "src and dst must be contiguous GPU tensors of the same byte size")
     _check(lib().fa_probe_copy(c_void_p(src.data_ptr()), c_void_p(dst.data_ptr()), n, _stream(stream)))
+
+
+def fa_probe_read(src, sink, stream=None):
+    """Read-only stream over src's bytes (a contiguous GPU tensor); sink: int32 GPU
+    tensor of >= min(8192, ceil(bytes / 16384)) elements."""
+    n = src.numel() * src.element_size()
+    _need(src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.element_size() == 4,
+          "src must be a contiguous GPU tensor and sink a 4-byte GPU tensor")
+    _check(lib().fa_probe_read(c_void_p(src.data_ptr()), n, c_void_p(sink.data_ptr()), sink.numel(), _stream(stream)))

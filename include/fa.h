@@ -301,12 +301,24 @@ fa_status fa_backward(const fa_attn_args* a, const fa_grad_args* g, void* worksp
  * published one (bf16 matrix peak, HBM bandwidth). */
 
 /* Dense bf16 MFMA loop: `workgroups` workgroups of 256 threads; every wave runs
- * `iterations` rounds of 8 independent v_mfma_f32_32x32x16_bf16 chains on
- * register operands (32768 flops per instruction).  *flops receives the flop
- * count of the launch; `sink` (device fp32, workgroups * 256 entries) receives
- * one value per lane so the work is not optimised away.
+ * `iterations` rounds (rounded up to even) of 8 independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands (32768 flops per
+ * instruction).  random_operands = 0: constant operands (the datapath hardly
+ * switches); 1: random bf16 signs and mantissas, two operand sets alternating
+ * between rounds (switching as on real data, which costs power).  *flops
+ * receives the flop count of the launch; `sink` (device fp32, workgroups * 256
+ * entries) receives one value per lane so the work is not optimised away.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE (workgroups or iterations < 1), FA_ERR_HIP. */
-fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, float* sink, double* flops, void* stream);
+fa_status fa_probe_mfma(int32_t workgroups, int32_t iterations, int32_t random_operands, float* sink, double* flops,
+                        void* stream);
+
+/* Read-only stream over `bytes` bytes at src (a device pointer, 16-byte
+ * aligned, bytes a multiple of 16): 16-byte loads, each byte read once, folded
+ * into one 32-bit word per workgroup written to `sink` (device, sink_words
+ * entries; the probe uses min(8192, ceil(bytes / 16384)) workgroups).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (bytes, or a sink too small), FA_ERR_UNSUPPORTED
+ * (alignment), FA_ERR_HIP. */
+fa_status fa_probe_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
 
 /* Streaming copy of `bytes` bytes from src to dst (device pointers, 16-byte
  * aligned, bytes a multiple of 16): 16-byte loads and stores, each byte read

@@ -343,13 +343,17 @@ def test_decode_accepts_only_position_free_masks_and_forward_rejects_q_pos():
 def test_probe_validation_codes():
     L = fa.lib()
     f = ctypes.c_double()
-    assert L.fa_probe_mfma(1, 1, None, ctypes.byref(f), None) == fa.FA_ERR_NULL
-    assert L.fa_probe_mfma(0, 1, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
-    assert L.fa_probe_mfma(1, 0, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_mfma(1, 1, 0, None, ctypes.byref(f), None) == fa.FA_ERR_NULL
+    assert L.fa_probe_mfma(0, 1, 0, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_mfma(1, 0, 1, 0x10000, ctypes.byref(f), None) == fa.FA_ERR_SHAPE
     assert L.fa_probe_copy(None, 0x10000, 16, None) == fa.FA_ERR_NULL
     assert L.fa_probe_copy(0x10000, 0x20000, 0, None) == fa.FA_ERR_SHAPE
     assert L.fa_probe_copy(0x10000, 0x20000, 24, None) == fa.FA_ERR_SHAPE
     assert L.fa_probe_copy(0x10008, 0x20000, 32, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_probe_read(None, 16, 0x20000, 1, None) == fa.FA_ERR_NULL
+    assert L.fa_probe_read(0x10000, 24, 0x20000, 1, None) == fa.FA_ERR_SHAPE
+    assert L.fa_probe_read(0x10008, 32, 0x20000, 1, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_probe_read(0x10000, 1 << 30, 0x20000, 8191, None) == fa.FA_ERR_SHAPE   # needs 8192 sink words
 
 
 def test_noalloc_decode_size_limit_is_checked_on_the_host():
