@@ -326,8 +326,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---- bwd_dkdv ------------------------------------------------------------------------
+// One 512-thread workgroup (8 waves, two per SIMD) per (b, hkv, 128-key tile).
+// Wave w and wave w + 4 own the same 32 keys (a lane per key) and split the
+// work of every 64-row query sub-step j in two halves around a barrier:
+//  * P role (waves 0-3): S = Q K^T, P = exp2(S' - LSE) with the mask and the
+//    rows past Sq zeroed, P mod'(S) to LDS (bf16); after the barrier
+//    dV^T += dO^T P.
+//  * dS role (waves 4-7): dP = dO V^T beside dK^T += Q^T dS of sub-step
+//    j - 1; after the barrier dS = P mod'(S) (dP - Delta) from the P role's
+//    copy, kept (bf16) for the next sub-step.
+// Each role holds one of K / V and one of the dK / dV accumulators, so both fit
+// in the registers of two waves per SIMD; the element-wise work of one wave of
+// a SIMD (P before the barrier, dS after it) runs beside the other's MFMAs.
+constexpr int kDkdvThreads = 512;
+
 template <int D, class Mask, class Score>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams P) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KS = D / 16;
@@ -335,18 +349,22 @@ void bwd_dkdv_kernel(BwdParams P) {
   constexpr int CPR = D / 8;
   constexpr int HB = 64;                 // query rows per sub-step
   constexpr int SPT = kBM / HB;
-  constexpr int NI = HB * CPR / 64 / 4;
+  constexpr int NI = HB * CPR / 64 / 4;  // 16-byte loads per wave of a Q or dO sub-tile (4 waves a tile)
   const FwdParams& p = P.f;
   // Q and dO sub-tiles, row-major with the row/transposed swizzle, 3-deep ring:
-  // step j reads sub-tile j (S, dP) and j - 1 (the delayed dV, dK products)
-  // while sub-tile j + 1 loads
+  // sub-step j reads stage j % 3 (and Q of j - 1) while j + 1 loads
   __shared__ __align__(16) uint16_t q_lds[3][HB * D];
   __shared__ __align__(16) uint16_t g_lds[3][HB * D];
   // base-2 LSE (first HB floats) and Delta (next HB) of the sub-tile's query rows
   __shared__ __align__(16) float ld_lds[3][2 * HB];
+  // P mod'(S) of the sub-step for the dS role: per wave, four groups of 64
+  // lanes x 16 bytes (elements 8 g .. 8 g + 7 of the lane)
+  __shared__ __align__(16) uint16_t p_lds[4][64 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;         // 32-key block of the wave
+  const bool ds_role = wave >= 4;  // uniform per wave
   const int lq = lane & 31, hh = lane >> 5;
   const int gi = lane >> 4, si = lane & 15;
 
@@ -358,20 +376,18 @@ void bwd_dkdv_kernel(BwdParams P) {
   const int hkv = bh % p.Hkv, b = bh / p.Hkv;
   const int k0 = kb * kBN;
 
-  // ---- this lane's key row: K and V as B operands ----
-  const int mykv = k0 + wave * 32 + lq;
+  // ---- this lane's key row: K (P role) or V (dS role) as B operands ----
+  const int mykv = k0 + kw * 32 + lq;
   const bool kv_ok = mykv < p.Skv;
   const bool kv_all = k0 + kBN <= p.Skv;  // every key of the block exists
   const int kvc = kv_ok ? mykv : p.Skv - 1;
-  bf16x8_t kreg[KS], vreg[KS];
+  bf16x8_t xreg[KS];
   {
-    const uint16_t* Kr = p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1] + (long long)kvc * p.ks[2];
-    const uint16_t* Vr = p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1] + (long long)kvc * p.vs[2];
+    const uint16_t* Xr = ds_role
+        ? p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1] + (long long)kvc * p.vs[2]
+        : p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1] + (long long)kvc * p.ks[2];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Kr + 16 * s + 8 * hh));
-      vreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Vr + 16 * s + 8 * hh));
-    }
+    for (int s = 0; s < KS; ++s) xreg[s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(Xr + 16 * s + 8 * hh));
   }
 
   // ---- the query tiles to visit: for each head of the group, its column lists ----
@@ -418,14 +434,15 @@ void bwd_dkdv_kernel(BwdParams P) {
     ch = 0;
   };
 
+  // Loads: the P-role waves bring the Q sub-tile, the dS-role waves the dO
+  // sub-tile (each 4 waves x NI loads), wave 0 the LSE / Delta rows.
   constexpr int RPI = 64 / CPR;
-  const int lrow = wave * RPI + lane / CPR;
+  const int lrow = kw * RPI + lane / CPR;
   const int kchunk = (lane % CPR) ^ rt_swizzle<D>(lrow);
-  const long long qsb = 2 * p.qs[2], gsb = 2 * P.dos[2];
-  const uint32_t q_voff = (uint32_t)(lrow * qsb + 16 * kchunk);
-  const uint32_t g_voff = (uint32_t)(lrow * gsb + 16 * kchunk);
+  const long long xsb = ds_role ? 2 * P.dos[2] : 2 * p.qs[2];
+  const uint32_t x_voff = (uint32_t)(lrow * xsb + 16 * kchunk);
   auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int r0) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf) + 16 * 64 * wave);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf) + 16 * 64 * kw);
     if (r0 + HB <= p.Sq) {
       const char* g0 = g + r0 * rsb;
 #pragma unroll
@@ -457,10 +474,13 @@ void bwd_dkdv_kernel(BwdParams P) {
   };
   auto issue = [&](const Sub& s, int j) {
     const int r0 = s.qs0;
-    const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)s.hq * p.qs[1]);
-    const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)s.hq * P.dos[1]);
-    issue_one(Qh, qsb, q_lds[j % 3], q_voff, r0);
-    issue_one(Gh, gsb, g_lds[j % 3], g_voff, r0);
+    if (ds_role) {
+      const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)s.hq * P.dos[1]);
+      issue_one(Gh, xsb, g_lds[j % 3], x_voff, r0);
+    } else {
+      const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)s.hq * p.qs[1]);
+      issue_one(Qh, xsb, q_lds[j % 3], x_voff, r0);
+    }
     if (wave == 0 && lane < 2 * HB / 4) {  // 16 bytes a lane; the workspace rows are padded
       const long long w0 = ((long long)b * p.Hq + s.hq) * P.sq_pad + r0 + 4 * (lane % (HB / 4));
       dma16((lane < HB / 4 ? P.ws_lse2 : P.ws_delta) + w0, lds_address(ld_lds[j % 3]));
@@ -484,44 +504,32 @@ void bwd_dkdv_kernel(BwdParams P) {
         (lds_bf16x4_t*)(uintptr_t)(base + 2 * (tthi[dt] + ks * 16 * D)));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  // this lane's four 16-byte groups in the P mod'(S) buffer
+  const uint32_t pbase = lds_address(p_lds[kw]) + 16 * lane;
+  auto p_addr = [&](int g) { return pbase + 1024 * g; };
 
-  f32x16_t dv[DT], dk[DT];
+  f32x16_t acc[DT];  // dV (P role) or dK (dS role)
 #pragma unroll
-  for (int i = 0; i < DT; ++i) {
-    dv[i] = f32x16_t{};
-    dk[i] = f32x16_t{};
-  }
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  for (int i = 0; i < DT; ++i) acc[i] = f32x16_t{};
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-  // Software pipeline: the element-wise work of sub-step j runs beside the
-  // dV / dK MFMAs of sub-step j - 1 (whose P and dS were kept), so the wave
-  // has independent MFMAs in flight while it computes P and dS.  Stage 2
-  // stands in for "sub-step -1" at j = 0: zeroed, with P = dS = 0.
-  {
-    u32x4_t* z0 = (u32x4_t*)q_lds[2];
-    u32x4_t* z1 = (u32x4_t*)g_lds[2];
-    for (int i = tid; i < HB * D / 8; i += kBwdThreads) z0[i] = z1[i] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  bf16x8_t pbo[4], dsbo[4];  // P and dS of the previous sub-step
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pbo[i] = dsbo[i] = bf16x8_t{};
-  auto dvdk_mfma = [&](uint32_t qb_prev, uint32_t gb_prev, int ks) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(gb_prev, dt, ks), pbo[ks], dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read(qb_prev, dt, ks), dsbo[ks], dk[dt], 0, 0, 0);
-    }
+  // dK^T += Q^T dS for a sub-step whose Q is at qb, dS in dsb; MFMA i is
+  // k-step i / DT (16 query rows), d block i % DT
+  bf16x8_t dsb[4];  // (dS role) dS of the last sub-step, bf16 B operands
+  auto dk_mfma = [&](uint32_t qb, int i, bf16x8_t (&tq)[2]) {
+    if (i + 1 < 4 * DT) tq[(i + 1) & 1] = tr_read(qb, (i + 1) % DT, (i + 1) / DT);
+    acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[i & 1], dsb[i / DT], acc[i % DT], 0, 0, 0);
   };
 
   // One sub-step; the ring stage j % 3 is a compile-time constant (the loop
   // below is unrolled by 3) so that every LDS read address is a per-lane
-  // register plus an immediate offset.
-  // Sub-step descriptors run two ahead: the list entry read for j + 2 in step j
-  // is in hand when step j + 1 issues its loads.
+  // register plus an immediate offset.  Sub-step descriptors run two ahead.
   Sub nxt{0, 0, false}, nx2{0, 0, false};
-  auto step = [&](int j, auto stage) {
+  // (the role is a compile-time constant of each copy, so the two roles'
+  // registers are allocated apart; both pass the same barriers)
+  auto step = [&](int j, auto stage, auto role) {
     constexpr int st = decltype(stage)::value, sp = (st + 2) % 3;
+    constexpr bool ds_role = decltype(role)::value;
     wait_vmcnt<0>();
     wait_lds_reads();
     __syncthreads();  // sub-step j landed; every wave is done with j - 2, whose stage j + 1 reuses
@@ -529,105 +537,123 @@ void bwd_dkdv_kernel(BwdParams P) {
     nxt = nx2;
     if (j + 1 < Jtot) issue(nxt, j + 1);
     if (j + 2 < Jtot) nx2 = describe();
-    const int hq = cur.hq, qs0 = cur.qs0;  // query head, first query row of the sub-step
-    const bool partial = cur.partial;
-    const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);  // (may branch: before the MFMAs)
-    const int qlast = p.Sq - 1 - (qs0 + 4 * hh);
-    const bool fix = partial | (qs0 + HB > p.Sq) | !kv_all;  // needs the zeroing pass below
-    const uint32_t qbase = lds_address(q_lds[st]), gbase = lds_address(g_lds[st]);
-    const uint32_t qprev = lds_address(q_lds[sp]), gprev = lds_address(g_lds[sp]);
-    // LSE and Delta of this lane's rows 8 (r / 4) + 4 hh + r % 4 (+32 per query
-    // block): runs of four, read from LDS where the element-wise pass needs them
-    const uint32_t ldb = lds_address(ld_lds[st]) + 16 * hh;
-
-    // Transposed operands of the delayed dV / dK MFMAs (sub-step j - 1, whose
-    // stage is already in LDS): MFMA i reads k-step i / (2 DT), d block
-    // (i / 2) % DT, dO^T for even i (dV) and Q^T for odd i (dK).  The first
-    // PFT are read now; each later one PFT MFMAs before its use.
-    constexpr int NM = 8 * DT, PFT = 4;
-    auto tr_op = [&](int i) { return tr_read((i & 1) ? qprev : gprev, (i >> 1) % DT, i / (2 * DT)); };
-    bf16x8_t tro[NM];
-#pragma unroll
-    for (int i = 0; i < PFT; ++i) tro[i] = tr_op(i);
-
-    // S = Q K^T and dP = dO V^T: rows are query rows, this lane's column is its key
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}}, dpacc[2] = {f32x16_t{}, f32x16_t{}};
-    // A operands read PF pairs ahead of their MFMAs (one wave per SIMD: nothing
-    // else hides the LDS latency)
-    constexpr int PF = 3;
-    auto rd_q = [&](int i) { return *(const lds_bf16x8_t*)(uintptr_t)(qbase + 2 * (aoff[i % KS] + (i / KS) * 32 * D)); };
-    auto rd_g = [&](int i) { return *(const lds_bf16x8_t*)(uintptr_t)(gbase + 2 * (aoff[i % KS] + (i / KS) * 32 * D)); };
-    bf16x8_t aq[2 * KS], ag[2 * KS];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      aq[i] = rd_q(i);
-      ag[i] = rd_g(i);
-    }
-    auto sdp_mfma = [&](int i) {  // k-step i % KS of query block i / KS
-      const int mt = i / KS, s = i % KS;
-      if (i + PF < 2 * KS) {
-        aq[i + PF] = rd_q(i + PF);
-        ag[i + PF] = rd_g(i + PF);
-      }
-      sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], kreg[s], sacc[mt], 0, 0, 0);
-      dpacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[i], vreg[s], dpacc[mt], 0, 0, 0);
+    const uint32_t gbase = lds_address(g_lds[st]);
+    const uint32_t qbase = lds_address(q_lds[st]);
+    constexpr int PF = 4;  // A-operand reads run PF MFMAs ahead
+    // S = Q K^T (P role) or dP = dO V^T (dS role): MFMA i is query block i % 2,
+    // k-step i / 2 (two accumulation chains)
+    const uint32_t abase = ds_role ? gbase : qbase;
+    auto rd_a = [&](int i) {
+      return *(const lds_bf16x8_t*)(uintptr_t)(abase + 2 * (aoff[i >> 1] + (i & 1) * 32 * D));
     };
-    // query block 0 now; block 1 beside the element-wise work of block 0 below
+    // (dS role, j > 0) one dK MFMA of sub-step j - 1 after each
+    f32x16_t sd[2] = {f32x16_t{}, f32x16_t{}};
+    {
+      static_assert(2 * KS == 4 * DT, "dP and dK MFMAs pair up");
+      const bool with_dk = ds_role && j > 0;  // (false at compile time for the P role)
+      const uint32_t qprev = lds_address(q_lds[sp]);
+      bf16x8_t aq[2 * KS], tq[2];
 #pragma unroll
-    for (int i = 0; i < KS; ++i) sdp_mfma(i);
-
-    // P and dS = P (dP - Delta) mod'(S) of sub-step j, in place of S and dP,
-    // with one MFMA of dV^T += dO^T P or dK^T += Q^T dS of sub-step j - 1 after
-    // every 32 / (8 DT) elements, and during query block 0 the S and dP
-    // products of block 1.  Element (mt, r): query row
-    // qs0 + 32 mt + 8 (r / 4) + 4 hh + r % 4 of this lane's key.
-    constexpr int EPM = 32 / (8 * DT);  // elements per dV / dK MFMA
-    constexpr int EPS = 16 / KS;        // elements per S / dP pair of block 1
-    f32x4_t l4, d4;
+      for (int i = 0; i < PF; ++i) aq[i] = rd_a(i);
+      // The P role runs at a raised wave priority through its first half: its
+      // S MFMAs then go first on the SIMD, and its element-wise pass (the
+      // longer of the two halves' critical paths) runs beside the dS role's
+      // dP and dK MFMAs.  (-4% time against equal priorities.)
+      if constexpr (!ds_role) __builtin_amdgcn_s_setprio(2);
+      if (with_dk) tq[0] = tr_read(qprev, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int mt = e >> 4, r = e & 15;
-      const int dr = 32 * mt + 8 * (r >> 2) + (r & 3);  // query row qs0 + 4 hh + dr
-      if ((r & 3) == 0) {
-        l4 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldb + 4 * (32 * mt + 8 * (r >> 2)));
-        d4 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldb + 4 * (HB + 32 * mt + 8 * (r >> 2)));
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i + PF < 2 * KS) aq[i + PF] = rd_a(i + PF);
+        sd[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], xreg[i >> 1], sd[i & 1], 0, 0, 0);
+        if (with_dk) dk_mfma(qprev, i, tq);
       }
-      const float sv = sacc[mt][r];
-      // functors that read memory get an in-bounds row past Sq (zeroed below)
-      const float pv = __builtin_amdgcn_exp2f(
-          Score::apply_col(scol, sv, Score::kReadsMemory ? min(dr, qlast) : dr) - l4[r & 3]);
-      dpacc[mt][r] = pv * (dpacc[mt][r] - d4[r & 3]) * Score::dmod_col(scol, sv);
-      sacc[mt][r] = pv;
-      if (e % EPM == EPM - 1) {
-        const int i = e / EPM, ks = i / (2 * DT), dt = (i >> 1) % DT;
-        if (i + PFT < NM) tro[i + PFT] = tr_op(i + PFT);
-        if (i & 1)
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], dsbo[ks], dk[dt], 0, 0, 0);
-        else
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], pbo[ks], dv[dt], 0, 0, 0);
-      }
-      if (mt == 0 && e % EPS == EPS - 1) sdp_mfma(KS + e / EPS);
     }
-    // Zero what the mask drops (partial tiles), rows past Sq and a key past Skv
-    if (fix) {
+    if constexpr (!ds_role) {
+      // ---- P role: P, P mod'(S) to LDS ----
+      const int hq = cur.hq, qs0 = cur.qs0;  // query head, first query row of the sub-step
+      const bool partial = cur.partial;
+      const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);
+      const int qlast = p.Sq - 1 - (qs0 + 4 * hh);
+      const bool fix = partial | (qs0 + HB > p.Sq) | !kv_all;  // needs the zeroing pass below
+      const uint32_t ldb = lds_address(ld_lds[st]) + 16 * hh;
+      // element (mt, r): query row qs0 + 32 mt + 8 (r / 4) + 4 hh + r % 4
+      float pm[2][16];
+      f32x4_t l4;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int mt = e >> 4, r = e & 15;
-        const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        bool keep = kv_ok && q < p.Sq;
-        if (partial) keep = keep && Mask::row(p.mask, b, hq, min(q, p.Sq - 1))(kvc);
-        sacc[mt][r] = keep ? sacc[mt][r] : 0.0f;
-        dpacc[mt][r] = keep ? dpacc[mt][r] : 0.0f;
+        const int dr = 32 * mt + 8 * (r >> 2) + (r & 3);
+        if ((r & 3) == 0)
+          l4 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldb + 4 * (32 * mt + 8 * (r >> 2)));
+        const float sv = sd[mt][r];
+        // functors that read memory get an in-bounds row past Sq (zeroed below)
+        const float pv = __builtin_amdgcn_exp2f(
+            Score::apply_col(scol, sv, Score::kReadsMemory ? min(dr, qlast) : dr) - l4[r & 3]);
+        pm[mt][r] = pv * Score::dmod_col(scol, sv);
+        sd[mt][r] = pv;
+      }
+      // Zero what the mask drops (partial tiles), rows past Sq and a key past Skv
+      if (fix) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const int mt = e >> 4, r = e & 15;
+          const int q = qs0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool keep = kv_ok && q < p.Sq;
+          if (partial) keep = keep && Mask::row(p.mask, b, hq, min(q, p.Sq - 1))(kvc);
+          sd[mt][r] = keep ? sd[mt][r] : 0.0f;
+          pm[mt][r] = keep ? pm[mt][r] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int mt = g >> 1, h8 = 8 * (g & 1);
+        bf16x8_t pmb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pmb[k] = (__bf16)pm[mt][h8 + k];
+        *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(g) = __builtin_bit_cast(u32x4_t, pmb);
       }
     }
-    // packed as bf16 B operands (k = query row): k-step g holds elements 8 g .. 8 g + 7
+    if constexpr (!ds_role) __builtin_amdgcn_s_setprio(0);  // (back to the dS role's)
+    wait_lds_reads();  // (lgkmcnt covers the LDS writes too)
+    __syncthreads();  // P mod'(S) of sub-step j is in LDS
+    if constexpr (!ds_role) {
+      // second half: dV^T += dO^T P; MFMA i is k-step i / DT (16 query rows),
+      // d block i % DT, its A operand (a transposed read) PFT MFMAs ahead
+      bf16x8_t bo[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int mt = g >> 1, h8 = 8 * (g & 1);
+      for (int g = 0; g < 4; ++g) {
+        const int mt = g >> 1, h8 = 8 * (g & 1);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pbo[g][k] = (__bf16)sacc[mt][h8 + k];
-        dsbo[g][k] = (__bf16)dpacc[mt][h8 + k];
+        for (int k = 0; k < 8; ++k) bo[g][k] = (__bf16)sd[mt][h8 + k];
+      }
+      constexpr int NM = 4 * DT, PFT = 4;
+      bf16x8_t tro[NM];
+#pragma unroll
+      for (int i = 0; i < PFT; ++i) tro[i] = tr_read(gbase, i % DT, i / DT);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i + PFT < NM) tro[i + PFT] = tr_read(gbase, (i + PFT) % DT, (i + PFT) / DT);
+        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], bo[i / DT], acc[i % DT], 0, 0, 0);
+      }
+    } else {
+      // second half: dS = P mod'(S) (dP - Delta) as bf16 B operands (k =
+      // query row): k-step g holds elements 8 g .. 8 g + 7
+      const uint32_t ldp = lds_address(ld_lds[st]) + 16 * hh + 4 * HB;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int mt = g >> 1, h8 = 8 * (g & 1);
+        const u32x4_t pm = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(g);
+        // elements h8 .. h8 + 7 are rows 2 h8 + {0..3} and 2 h8 + 8 + {0..3} of the block (+ 4 hh)
+        const f32x4_t d0 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8));
+        const f32x4_t d1 =
+            *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8 + 8));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t w = pm[k >> 1];
+          const float pv = bf16_bits_to_float((k & 1) ? (w >> 16) : (w & 0xffffu));
+          const float dl = (k < 4) ? d0[k] : d1[k - 4];
+          dsb[g][k] = (__bf16)(pv * (sd[mt][h8 + k] - dl));
+        }
       }
     }
   };
@@ -636,33 +662,38 @@ void bwd_dkdv_kernel(BwdParams P) {
     issue(nxt, 0);
   }
   if (Jtot > 1) nx2 = describe();
-  for (int j = 0; j < Jtot; j += 3) {
-    step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < Jtot) step(j + 1, std::integral_constant<int, 1>{});
-    if (j + 2 < Jtot) step(j + 2, std::integral_constant<int, 2>{});
-  }
-  if (Jtot > 0) {  // the last sub-step's dV / dK (its stage is still intact)
-    const uint32_t ql = lds_address(q_lds[(Jtot - 1) % 3]), gl = lds_address(g_lds[(Jtot - 1) % 3]);
+  auto run = [&](auto role) {
+    for (int j = 0; j < Jtot; j += 3) {
+      step(j, std::integral_constant<int, 0>{}, role);
+      if (j + 1 < Jtot) step(j + 1, std::integral_constant<int, 1>{}, role);
+      if (j + 2 < Jtot) step(j + 2, std::integral_constant<int, 2>{}, role);
+    }
+  };
+  if (ds_role)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+  if (Jtot > 0 && ds_role) {  // dK of the last sub-step (its Q stage is still intact)
+    const uint32_t ql = lds_address(q_lds[(Jtot - 1) % 3]);
+    bf16x8_t tq[2];
+    tq[0] = tr_read(ql, 0, 0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dvdk_mfma(ql, gl, g);
+    for (int i = 0; i < 4 * DT; ++i) dk_mfma(ql, i, tq);
   }
 
-  if (kv_ok) {
-    const float sc = p.score.scale;
-    uint16_t* Gk = P.dk + (long long)b * P.dks[0] + (long long)hkv * P.dks[1] + (long long)mykv * P.dks[2];
-    uint16_t* Gv = P.dv + (long long)b * P.dvs[0] + (long long)hkv * P.dvs[1] + (long long)mykv * P.dvs[2];
+  if (kv_ok) {  // dV from the P role, dK (times the scale) from the dS role
+    const float sc = ds_role ? p.score.scale : 1.0f;
+    uint16_t* G = ds_role
+        ? P.dk + (long long)b * P.dks[0] + (long long)hkv * P.dks[1] + (long long)mykv * P.dks[2]
+        : P.dv + (long long)b * P.dvs[0] + (long long)hkv * P.dvs[1] + (long long)mykv * P.dvs[2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4_t k4, v4;
+        bf16x4_t o4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          k4[i] = (__bf16)(dk[dt][4 * g + i] * sc);
-          v4[i] = (__bf16)dv[dt][4 * g + i];
-        }
-        *(bf16x4_t*)(Gk + 32 * dt + 8 * g + 4 * hh) = k4;
-        *(bf16x4_t*)(Gv + 32 * dt + 8 * g + 4 * hh) = v4;
+        for (int i = 0; i < 4; ++i) o4[i] = (__bf16)(acc[dt][4 * g + i] * sc);
+        *(bf16x4_t*)(G + 32 * dt + 8 * g + 4 * hh) = o4;
       }
     }
   }
@@ -679,7 +710,7 @@ struct LaunchBwd {
     hipLaunchKernelGGL((bwd_dq_kernel<D, Mask, Score>), dim3((unsigned)(NQ * p.Hq * p.B)), dim3(kBwdThreads), 0,
                        stream, P);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, Mask, Score>), dim3((unsigned)(NK * p.Hkv * p.B)),
-                       dim3(kBwdThreads), 0, stream, P);
+                       dim3(kDkdvThreads), 0, stream, P);
   }
 };
 
