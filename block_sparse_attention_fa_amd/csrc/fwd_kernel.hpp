@@ -151,7 +151,12 @@ void fwd_kernel(FwdParams p) {
   __shared__ __align__(16) uint16_t k_lds[NK][HB * D];
   __shared__ __align__(16) uint16_t v_lds[NV][HB * D];
   // Bias tiles [128 query rows x 64 keys] of steps j and j+1 (only for the
-  // staged bias): row r holds its 8 16-byte chunks c at slot c ^ (r % 8).
+  // staged bias): row r holds its 8 16-byte chunks c at slot c ^ ((r / 2) % 8),
+  // so that of the 32 rows one half-wave reads at a time, 16 fall on distinct
+  // bank groups (2-way conflicts where the plain c ^ (r % 8) had 4-way).  Each
+  // wave loads and reads only its own 32 rows, so a stage is free again for the
+  // wave once it has read it, and the tile of step j+2 goes into the stage of
+  // step j with no barrier.
   constexpr bool BL = Score::kStagesBias;
   __shared__ __align__(16) uint16_t b_lds[BL ? 2 : 1][BL ? kBM * HB : 8];
   // Document ids of sub-tiles j, j+1, j+2 (masks that read them, D = 64, where
@@ -264,33 +269,36 @@ void fwd_kernel(FwdParams p) {
     }
   };
   auto issue_v = [&](int j) { issue_one(Vp, vsb, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
-  // Bias tile of sub-tile j -> b_lds[j % 2]: wave w issues slots 64 (4i + w) + lane
-  // (i < 4), i.e. row 32 i + 8 w + lane / 8, stored slot lane % 8 holding chunk
-  // bc = (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
-  const int b_row = 8 * wave + (lane >> 3);  // + 32 i
-  const int bc = (lane & 7) ^ ((lane >> 3) & 7);
+  // Bias tile of sub-tile j -> b_lds[j % 2]: wave w issues slots 64 (4w + i) + lane
+  // (i < 4), i.e. row 32 w + 8 i + lane / 8, stored slot lane % 8 holding chunk
+  // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ (lane / 16) ^ (4 (i % 2)).
+  const int b_row = lane >> 3;  // + 32 w + 8 i
+  const int bc0 = (lane & 7) ^ (lane >> 4);  // chunk for even i (odd i: bc0 ^ 4)
   const char* Bbh = nullptr;
   long long bsb = 0;  // bias row stride in bytes
-  uint32_t b_voff = 0;
+  uint32_t b_voff0 = 0, b_voff1 = 0;
   if constexpr (BL) {
     Bbh = (const char*)(p.score.bias + (long long)b * p.score.bs0 + (long long)hq * p.score.bs1);
     bsb = 2 * p.score.bs2;
-    b_voff = (uint32_t)(b_row * bsb + 16 * bc);
+    b_voff0 = (uint32_t)(b_row * bsb + 16 * bc0);
+    b_voff1 = (uint32_t)(b_row * bsb + 16 * (bc0 ^ 4));
   }
+  constexpr int NB = 4;  // bias loads per wave per sub-tile
   auto issue_b = [&](int j) {
     if constexpr (BL) {
       const int kv0 = kv0_of(j);
-      const uint32_t base = lds_address(b_lds[j % 2]) + 16 * 64 * wave;
-      if (q0 + kBM <= p.Sq && kv0 + HB <= p.Skv) {
-        const char* g0 = Bbh + (long long)q0 * bsb + 2 * kv0;
+      const uint32_t base = lds_address(b_lds[j % 2]) + 16 * 64 * 4 * wave;
+      const int r0 = q0 + 32 * wave;  // first row of the wave
+      if (r0 + 32 <= p.Sq && kv0 + HB <= p.Skv) {
+        const char* g0 = Bbh + (long long)r0 * bsb + 2 * kv0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16s(b_voff, g0 + 32 * i * bsb, base + 16 * 64 * 4 * i);
+        for (int i = 0; i < NB; ++i) dma16s((i & 1) ? b_voff1 : b_voff0, g0 + 8 * i * bsb, base + 16 * 64 * i);
       } else {  // ragged: clamp rows to Sq-1 and chunks to the last one of the row
-        const int kc = min(kv0 + 8 * bc, p.Skv - 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = min(q0 + 32 * i + b_row, p.Sq - 1);
-          dma16(Bbh + (long long)q * bsb + 2 * kc, base + 16 * 64 * 4 * i);
+        for (int i = 0; i < NB; ++i) {
+          const int q = min(r0 + 8 * i + b_row, p.Sq - 1);
+          const int kc = min(kv0 + 8 * (bc0 ^ (4 * (i & 1))), p.Skv - 8);
+          dma16(Bbh + (long long)q * bsb + 2 * kc, base + 16 * 64 * i);
         }
       }
     }
@@ -392,12 +400,17 @@ void fwd_kernel(FwdParams p) {
       u32x4_t* vz = (u32x4_t*)v_lds[NV - 1];
       for (int i = tid; i < HB * D / 8; i += kFwdThreads) vz[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    // The bias tile of sub-tile j is issued two steps ahead (in step j-2, once
+    // the wave has read its rows of that stage); in the issue order it sits
+    // after K(j) and V(j-1).
+    constexpr int NBI = BL ? NB : 0;
     issue_k(0);
     issue_b(0);
     if (J > 1) issue_k(1);
     issue_v(0);
+    if (J > 1) issue_b(1);
     if (J > 1)
-      wait_vmcnt<2 * NI>();  // K(0) (and the bias of 0) landed (K(1), V(0) may be in flight)
+      wait_vmcnt<2 * NI + NBI>();  // K(0) and the bias of 0 landed (K(1), V(0), bias of 1 may be in flight)
     else
       wait_vmcnt<NI>();
     wait_lds_reads();
@@ -414,9 +427,13 @@ void fwd_kernel(FwdParams p) {
     f32x16_t (&s_nxt)[2] = s_b;
     for (int j = 0; j < J; ++j) {
       const int H = j % SPT;
-      // K(j+1) and V(j-1) landed for every wave (only V(j) may be in flight), and
-      // every wave is done with step j-1: K stage j % 2 and V stage (j+1) % 3 are free.
-      wait_vmcnt<NI>();
+      // K(j+1), V(j-1) and the bias of j landed for every wave (only V(j) and
+      // the bias of j+1 may be in flight), and every wave is done with step
+      // j-1: K stage j % 2 and V stage (j+1) % 3 are free.
+      if (j + 1 < J)
+        wait_vmcnt<NI + NBI>();
+      else
+        wait_vmcnt<NI>();
       wait_lds_reads();
       __builtin_amdgcn_s_barrier();
       const int t = j / SPT;
@@ -426,10 +443,7 @@ void fwd_kernel(FwdParams p) {
         loaded(win);
       }
       if (j + 2 < J) issue_k(j + 2);
-      if (j + 1 < J) {
-        issue_b(j + 1);  // before V(j+1), so "only V in flight" also covers it
-        issue_v(j + 1);
-      }
+      if (j + 1 < J) issue_v(j + 1);
 
       const int kvt0 = kb_of(t) * kBN + HB * H;
       const bool partial = t < n_part;
@@ -451,9 +465,16 @@ void fwd_kernel(FwdParams p) {
         const uint32_t rowa = lds_address(b_lds[j % 2]) + 128 * br + 8 * hh;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
-          const uint64_t w = *(const __attribute__((address_space(3))) uint64_t*)(uintptr_t)(rowa + 16 * (g ^ (br & 7)));
+          const uint64_t w =
+              *(const __attribute__((address_space(3))) uint64_t*)(uintptr_t)(rowa + 16 * (g ^ ((br >> 1) & 7)));
           bias2[g][0] = (uint32_t)w;
           bias2[g][1] = (uint32_t)(w >> 32);
+        }
+        // once the wave's rows are in registers (the first LDS reads of the
+        // step: nothing else to wait for), its stage takes the tile of j+2
+        if (j + 2 < J) {
+          wait_lds_reads();
+          issue_b(j + 2);
         }
       }
 #pragma unroll
@@ -478,50 +499,60 @@ void fwd_kernel(FwdParams p) {
       // alone, the compiler moves it (and a copy of every score register) past
       // the masked-pass branch, where no MFMA is in flight to cover it.
       if constexpr (!Score::kBounded) asm volatile("" : "+v"(ymax));
+
       if (partial || ragged) {  // mask_mod on partial tiles, keys past Skv on the ragged tile
         const auto mtl = Mask::tile(mrow, kvb);
         ymax = -INFINITY;
-        // A mask that reads memory (document ids) is evaluated for every element
-        // first, in-bounds and without branches, so all its loads are in flight
-        // at once; the others are evaluated where needed.
-        // Document ids come in runs of 4 keys (16 bytes) per lane: one vector
-        // load each when the ids are 16-byte aligned and the tile is whole.
-        bool mk[32];
-        if constexpr (Mask::kReadsMemory) {
-          if (DL && p.mask.doc_vec && !ragged) {
-            typedef int i32x4_t __attribute__((ext_vector_type(4)));
-            const uint32_t ids0 = lds_address(doc_lds[DL ? j % 3 : 0]) + 16 * hh;  // keys kvb = kvt0 + 4 hh
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {  // keys kvb + 32 (g / 4) + 8 (g % 4) + {0..3}
-              const int cr = 32 * (g >> 2) + 8 * (g & 3);
-              const i32x4_t v = *(const __attribute__((address_space(3))) i32x4_t*)(uintptr_t)(ids0 + 4 * cr);
-              const int ids[4] = {v[0], v[1], v[2], v[3]};
-              bool k4[4];
-              Mask::keep4(mtl, cr, ids, k4);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) mk[4 * g + i] = k4[i];
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-              const int mt = e >> 4, r = e & 15;
-              mk[e] = Mask::keep(mtl, min(32 * mt + 8 * (r >> 2) + (r & 3), lim - 1));
-            }
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
+        auto put = [&](int e, bool keep) {  // element e kept or set to -inf, and the row max
           const int mt = e >> 4, r = e & 15;
-          const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
-          bool keep = cr < lim;
-          if constexpr (Mask::kReadsMemory) {
-            keep = keep && (mk[e] || !partial);
-          } else {
-            if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
-          }
           const float y = keep ? s_cur[mt][r] : -INFINITY;
           s_cur[mt][r] = y;
           if constexpr (!Score::kBounded) ymax = fmaxf(ymax, y);
+        };
+        if (Mask::kReadsMemory && DL && p.mask.doc_vec && !ragged) {
+          // Document ids from LDS in runs of 4 keys (16 bytes) per lane: all 8
+          // runs are read first, then every element is decided and applied at
+          // once (a whole tile here, so only the mask decides; a partial tile,
+          // since the tile is not ragged).
+          typedef int i32x4_t __attribute__((ext_vector_type(4)));
+          const uint32_t ids0 = lds_address(doc_lds[DL ? j % 3 : 0]) + 16 * hh;  // keys kvb = kvt0 + 4 hh
+          i32x4_t v[8];
+#pragma unroll
+          for (int g = 0; g < 8; ++g)  // keys kvb + 32 (g / 4) + 8 (g % 4) + {0..3}
+            v[g] = *(const __attribute__((address_space(3))) i32x4_t*)(uintptr_t)(ids0 + 4 * (32 * (g >> 2) + 8 * (g & 3)));
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {  // elements 4 g .. 4 g + 3
+            const int ids[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
+            bool k4[4];
+            Mask::keep4(mtl, 32 * (g >> 2) + 8 * (g & 3), ids, k4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) put(4 * g + i, k4[i]);
+          }
+        } else if constexpr (Mask::kReadsMemory) {
+          // A mask that reads memory (document ids) from global memory is
+          // evaluated for every element first, in-bounds and without branches,
+          // so all its loads are in flight at once.
+          bool mk[32];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int mt = e >> 4, r = e & 15;
+            mk[e] = Mask::keep(mtl, min(32 * mt + 8 * (r >> 2) + (r & 3), lim - 1));
+          }
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int mt = e >> 4, r = e & 15;
+            const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+            put(e, cr < lim && (mk[e] || !partial));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int mt = e >> 4, r = e & 15;
+            const int cr = 32 * mt + 8 * (r >> 2) + (r & 3);
+            bool keep = cr < lim;
+            if (partial) keep = keep && Mask::keep(mtl, min(cr, lim - 1));
+            put(e, keep);
+          }
         }
       }
 #pragma unroll
