@@ -520,13 +520,27 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int g = 0; g < 8; ++g)  // keys kvb + 32 (g / 4) + 8 (g % 4) + {0..3}
             v[g] = *(const __attribute__((address_space(3))) i32x4_t*)(uintptr_t)(ids0 + 4 * (32 * (g >> 2) + 8 * (g & 3)));
+          // (wave-uniform: the parts that read no memory, e.g. causal, decide
+          // nothing on the wave's rows x this sub-tile's keys)
+          const int wq0 = min(q0 + 32 * wave, p.Sq - 1), wq1 = min(q0 + 32 * wave + 31, p.Sq - 1);
+          if (MaskParts<Mask>::rest_full(p.mask, b, hq, wq0, wq1, kvt0, kvt0 + HB - 1)) {
 #pragma unroll
-          for (int g = 0; g < 8; ++g) {  // elements 4 g .. 4 g + 3
-            const int ids[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
-            bool k4[4];
-            Mask::keep4(mtl, 32 * (g >> 2) + 8 * (g & 3), ids, k4);
+            for (int g = 0; g < 8; ++g) {  // elements 4 g .. 4 g + 3
+              const int ids[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
+              bool k4[4];
+              MaskParts<Mask>::keep4_mem(mtl, 32 * (g >> 2) + 8 * (g & 3), ids, k4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) put(4 * g + i, k4[i]);
+              for (int i = 0; i < 4; ++i) put(4 * g + i, k4[i]);
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+              const int ids[4] = {v[g][0], v[g][1], v[g][2], v[g][3]};
+              bool k4[4];
+              Mask::keep4(mtl, 32 * (g >> 2) + 8 * (g & 3), ids, k4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) put(4 * g + i, k4[i]);
+            }
           }
         } else if constexpr (Mask::kReadsMemory) {
           // A mask that reads memory (document ids) from global memory is
