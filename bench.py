@@ -182,22 +182,41 @@ class Timer:
         self.stream = stream
         self.power = power
         self.last_power = None
+        self.last_stats = None
         self.e0 = torch.cuda.Event(enable_timing=True)
         self.e1 = torch.cuda.Event(enable_timing=True)
 
-    def ms(self, fn, calls, untimed):
+    def ms(self, fn, calls, untimed, per_call=False):
+        """Mean ms per call over `calls` back-to-back calls after `untimed` ones.
+        With per_call, an event is also recorded between calls, and the median
+        and minimum per call go to self.last_stats."""
         import torch
         for _ in range(untimed):
             fn()
         torch.cuda.synchronize()
-        self.e0.record(self.stream)
-        for _ in range(calls):
-            fn()
-        self.e1.record(self.stream)
-        torch.cuda.synchronize()
+        if per_call:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+            evs[0].record(self.stream)
+            for i in range(calls):
+                fn()
+                evs[i + 1].record(self.stream)
+            torch.cuda.synchronize()
+            each = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(calls))
+            total = evs[0].elapsed_time(evs[calls])
+            self.last_stats = {"median_ms": round(each[calls // 2] if calls % 2 else
+                                                  0.5 * (each[calls // 2 - 1] + each[calls // 2]), 4),
+                               "min_ms": round(each[0], 4), "calls": calls}
+        else:
+            self.e0.record(self.stream)
+            for _ in range(calls):
+                fn()
+            self.e1.record(self.stream)
+            torch.cuda.synchronize()
+            total = self.e0.elapsed_time(self.e1)
+            self.last_stats = None
         if self.power:
             self.last_power = sample_power(fn)
-        return self.e0.elapsed_time(self.e1) / calls
+        return total / calls
 
 
 def leg_peaks(T, dev):
@@ -263,7 +282,7 @@ def leg_tiny(T, dev):
 def _fwd_leg(T, q, k, v, bm, score, calls, settle):
     out = q.new_empty(q.shape)
     from block_sparse_attention_fa_amd import fa
-    return T.ms(lambda: fa.fa_forward(q, k, v, block_mask=bm, score=score, out=out), calls, settle), out
+    return T.ms(lambda: fa.fa_forward(q, k, v, block_mask=bm, score=score, out=out), calls, settle, per_call=True), out
 
 
 def leg_sliding(T, dev, peaks):
@@ -279,13 +298,13 @@ def leg_sliding(T, dev, peaks):
     flops = 4.0 * D * n_att
     tf = flops / (ms * 1e-3) / 1e12
     n_part, n_full = int((cls == 1).sum()), int((cls == 2).sum())
-    return {"workload": c["name"], "kernel_ms": round(ms, 4), "attended_tflops": round(tf, 2),
+    return {"workload": c["name"], "kernel_ms": round(ms, 4), "per_call": T.last_stats, "attended_tflops": round(tf, 2),
             "attended_flops": flops, "power": T.last_power if T.power else None,
             "tiles_partial": n_part, "tiles_full": n_full,
             "executed_tile_tflops": round(4.0 * D * 128 * 128 * (n_part + n_full) * B * H / (ms * 1e-3) / 1e12, 2),
             "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", peaks.get("mfma_bf16_tflops"),
                                  read_traffic("fwd_sliding_softcap_16384_traffic.md", SLIDE_SOURCES),
-                                 kernel="fwd_kernel<128, MaskSlidingCausal, ScoreSoftcap>",
+                                 kernel="fwd_kernel<128, MaskAnd<MaskCausal, MaskWindow>, ScoreSoftcapBounded>",
                                  algorithmic_bytes=4 * B * H * S * D * 2)}
 
 
@@ -311,6 +330,7 @@ def leg_document(T, dev, peaks):
     bm = fa.fa_build_block_mask(mask, B, 1, S, S, device=dev)
     cls = bm.classes()
     ms, _ = _fwd_leg(T, q, k, v, bm, fa.ScoreMod("bias", bias=bias), 20, 30)
+    doc_stats = T.last_stats
     lens = np.concatenate([np.bincount(docs[b]) for b in range(B)]).astype(np.int64)
     n_att = H * int((lens * (lens + 1) // 2).sum())          # document AND causal: L(L+1)/2 per document
     n_part, n_full = int((cls == 1).sum()), int((cls == 2).sum())
@@ -320,7 +340,7 @@ def leg_document(T, dev, peaks):
     tile_bias = 2 * 128 * 128 * (n_part + n_full) * H       # bias bytes of every visited tile
     del bias
     torch.cuda.empty_cache()
-    return {"workload": c["name"], "kernel_ms": round(ms, 4), "documents": int(lens.size),
+    return {"workload": c["name"], "kernel_ms": round(ms, 4), "per_call": doc_stats, "documents": int(lens.size),
             "power": T.last_power if T.power else None,
             "attended_tflops": round(4.0 * D * n_att / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(4.0 * D * n_att / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -329,7 +349,7 @@ def leg_document(T, dev, peaks):
             "block_granular_gbs": round((qkvo + tile_bias) / (ms * 1e-3) / 1e9, 1),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", peaks.get("read_gbs"),
                                  read_traffic("fwd_document_bias_16384_traffic.md", DOC_SOURCES),
-                                 kernel="fwd_kernel<64, MaskDocumentCausal, ScoreBiasTiled>",
+                                 kernel="fwd_kernel<64, MaskAnd<MaskDocument, MaskCausal>, ScoreBiasTiled>",
                                  bytes_definition="Q, K, V read and O written once + the bf16 bias at attended positions")}
 
 
@@ -353,11 +373,13 @@ def leg_decode(T, dev, peaks, stream):
     sc = fa.ScoreMod("softcap", softcap=DEC["cap"])
     ws = torch.empty(fa.fa_decode_workspace_size(qdt, kct, vct, bmd, sc) // 4 + 1, dtype=torch.float32, device=dev)
     calls, settle = 50, 30
-    dec_ms = T.ms(lambda: fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws), calls, settle)
+    dec_ms = T.ms(lambda: fa.fa_decode(qdt, kct, vct, block_mask=bmd, score=sc, out=od, workspace=ws), calls, settle,
+                  per_call=True)
+    dec_stats = T.last_stats
     kv_bytes = int(lens.astype(np.int64).sum()) * Hkv * Dd * 2 * 2
     dec_bytes = kv_bytes + 2 * Bd * Hq * Dd * 2
     gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
-    res = {"workload": DEC["name"], "ms": round(dec_ms, 4), "GB/s": round(gbs, 1),
+    res = {"workload": DEC["name"], "ms": round(dec_ms, 4), "per_call": dec_stats, "GB/s": round(gbs, 1),
            "power": T.last_power if T.power else None,
            "untimed_calls": settle, "timed_calls": calls, "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
            "algorithmic_bytes": dec_bytes,
@@ -412,10 +434,11 @@ def leg_backward(T, dev, qt, kt, vt):
                       dtype=torch.float32, device=dev)
     settle, calls = 30, 10
     ms = T.ms(lambda: fa.fa_backward(qt, kt, vt, out, lse, dot, block_mask=bmt, score=score, dq=dq, dk=dk, dv=dv,
-                                     workspace=wsb), calls, settle)
+                                     workspace=wsb), calls, settle, per_call=True)
     n_att = B * H * S * (S + 1) // 2
     tf = 10.0 * D * n_att / (ms * 1e-3) / 1e12
-    return {"workload": "backward of " + FWD["name"], "ms": round(ms, 4), "attended_tflops": round(tf, 2),
+    return {"workload": "backward of " + FWD["name"], "ms": round(ms, 4), "per_call": T.last_stats,
+            "attended_tflops": round(tf, 2),
             "power": T.last_power if T.power else None,
             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "flops_per_attended_position": "10*D (S, dP, dV, dK, dQ products)",
@@ -598,7 +621,11 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         step_ms = (t1 - t0) * 1e3 / args.steps
-        fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        each = sorted(a.elapsed_time(b) for a, b in evs)
+        fwd_ms = sum(each) / args.steps
+        fwd_stats = {"median_ms": round(each[len(each) // 2] if len(each) % 2 else
+                                        0.5 * (each[len(each) // 2 - 1] + each[len(each) // 2]), 4),
+                     "min_ms": round(each[0], 4), "calls": len(each)}
         main_power = sample_power(step) if args.power else None
         build_ms = T.ms(lambda: fa._check(L.fa_build_block_mask(ctypes.byref(bm.c), S, S, sptr)), 10, 0)
         cls = bm.classes()
@@ -617,7 +644,8 @@ def main():
             "config": {"workload": FWD["name"], "B": B, "H": H, "S": S, "D": D, "mask": "causal",
                        "score_mod": "alibi", "block": 128, "step": "fa_build_block_mask + fa_forward",
                        "legs_before_timed_step": [x for x in legs if x != "main"]},
-            "fwd": {"kernel_ms": round(fwd_ms, 4), "attended_tflops": round(fwd_tflops, 2), "power": main_power,
+            "fwd": {"kernel_ms": round(fwd_ms, 4), "per_call": fwd_stats, "attended_tflops": round(fwd_tflops, 2),
+                    "power": main_power,
                     "frac_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                     "executed_tile_tflops": round(exec_flops / (fwd_ms * 1e-3) / 1e12, 2),
                     "tiles_partial": n_part, "tiles_full": n_full, "blockmask_build_ms": round(build_ms, 4),
