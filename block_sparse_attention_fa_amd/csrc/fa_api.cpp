@@ -26,6 +26,7 @@ fa_status fail(fa_status s, const char* fmt, ...) {
 }
 
 constexpr float kLog2eHost = 1.4426950408889634f;
+constexpr int64_t kMaxRowStride = (int64_t)1 << 25;  // K/V row strides in elements (64 MiB)
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -99,6 +100,9 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
   if ((st = check_strides("k", a->k_stride, a->k)) != FA_OK) return st;
   if ((st = check_strides("v", a->v_stride, a->v)) != FA_OK) return st;
   if ((st = check_strides("o", a->o_stride, a->o)) != FA_OK) return st;
+  // the kernels address the rows of a 64-key K/V sub-tile with 32-bit offsets
+  if (a->k_stride[2] >= kMaxRowStride || a->v_stride[2] >= kMaxRowStride)
+    return fail(FA_ERR_UNSUPPORTED, "k/v row stride must be below %lld elements", (long long)kMaxRowStride);
   if (!(isfinite(a->scale)) || a->scale < 0.0f) return fail(FA_ERR_SHAPE, "scale must be finite and >= 0");
   if (a->scale > 0.0f && a->scale < 1e-20f) return fail(FA_ERR_SHAPE, "scale must be 0 (default) or >= 1e-20");
 

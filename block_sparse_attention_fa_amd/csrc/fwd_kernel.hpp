@@ -27,10 +27,20 @@
 // of the 8-byte row pointed to by lane 4j + i/4 (j = 0..3), so lanes pointing
 // at a 4-key x 16-dim block of V receive one dim each across the 4 keys.
 //
-// Software pipeline.  On gfx950 a wave's VALU work only overlaps MFMAs that
-// the same wave has in flight (measured: none across waves of a SIMD), so
-// each 64-key step pairs the score VALU of sub-tile j with the PV MFMAs of
-// sub-tile j-1, and the exponentials of j with the QK^T MFMAs of j+1.
+// Software pipeline.  Step j of a wave does the PV product of sub-tile j-1,
+// the QK^T product of sub-tile j+1 and the softmax of sub-tile j, in one of
+// two orders (chosen per score at compile time):
+//  * phased (scores of a few VALU operations per element): the 32 MFMAs of the
+//    step first, back to back at raised wave priority with their LDS operands
+//    read four MFMAs ahead, then the softmax VALU at normal priority.  The two
+//    waves of a SIMD come from different workgroups: while one is in its MFMA
+//    stretch the other's VALU issues beside it, and the priority lets the
+//    MFMAs go first whenever both are ready.  A wave that mixed the two would
+//    hold its own VALU behind every MFMA that waits for the matrix pipe.
+//  * interleaved (softcap, with two more transcendentals per score, and the
+//    dynamic bias, whose LDS tile reads would sit in the VALU stretch): the
+//    score VALU of j beside the PV MFMAs of j-1, the exponentials of j beside
+//    the QK^T MFMAs of j+1, so a wave's own MFMAs cover its VALU.
 //
 // Data movement: K and V sub-tiles go from global memory straight into LDS
 // with 16-byte global_load_lds (no registers), row-major with the 16-byte
@@ -95,11 +105,19 @@ __device__ __forceinline__ uint32_t lds_address(const void* ptr) {
 // DMA), which is declared clobbered.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(lds) : "m0");
+               :: "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "m0");
 }
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds) : "m0");
+               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "m0");
+}
+// N loads of 16 bytes per lane into LDS at lds + 4096 i + 16 lane (i < N), from
+// sbase + voff[i]: one uniform base and a per-lane offset per load, so a tile's
+// loads cost one scalar address for the tile and an M0 write per load.
+template <int N>
+__device__ __forceinline__ void dma16n(const uint32_t (&voff)[N], const void* sbase, uint32_t lds) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) dma16s(voff[i], sbase, lds + 4096 * i);
 }
 
 // LDS swizzles (16-byte chunk index XOR a function of the row), chosen per
@@ -148,6 +166,8 @@ void fwd_kernel(FwdParams p) {
   constexpr int SPT = kBN / HB;               // steps per BlockMask tile
   constexpr int NI = HB * CPR / 64 / 4;       // 16-byte loads per wave per K or V sub-tile
   constexpr int NK = 2, NV = 3;               // ring depths: K of j+1 / j+2, V of j-1 / j / j+1
+  // phased or interleaved step (see the header)
+  constexpr bool PH = D == 128 && !Score::kReadsMemory && !std::is_base_of<ScoreSoftcap, Score>::value;
   __shared__ __align__(16) uint16_t k_lds[NK][HB * D];
   __shared__ __align__(16) uint16_t v_lds[NV][HB * D];
   // Bias tiles [128 query rows x 64 keys] of steps j and j+1 (only for the
@@ -236,14 +256,20 @@ void fwd_kernel(FwdParams p) {
   const int lrow = wave * RPI + lane / CPR;
   const int kchunk = (lane % CPR) ^ k_swizzle<D>(lrow);
   const int vchunk = (lane % CPR) ^ v_swizzle<D>(lrow);
-  const uint32_t k_voff = (uint32_t)(lrow * ksb + 16 * kchunk);
-  const uint32_t v_voff = (uint32_t)(lrow * vsb + 16 * vchunk);
-  auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, int lchunk, uint32_t voff, int kv0) {
+  // per-lane byte offsets of the wave's NI loads inside a sub-tile (row strides
+  // below 2^26 bytes are checked by the host, so they fit 32 bits)
+  const uint32_t ksb32 = (uint32_t)ksb, vsb32 = (uint32_t)vsb;
+  uint32_t k_vo[NI], v_vo[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    k_vo[i] = (uint32_t)(lrow + 4 * RPI * i) * ksb32 + 16 * kchunk;
+    v_vo[i] = (uint32_t)(lrow + 4 * RPI * i) * vsb32 + 16 * vchunk;
+  }
+  auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, int lchunk, const uint32_t (&vo)[NI], int kv0) {
     const uint32_t base = lds_address(buf) + 16 * 64 * wave;
     if (kv0 + HB <= p.Skv) {
-      const char* g0 = g + kv0 * rsb;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) dma16s(voff, g0 + 4 * RPI * i * rsb, base + 16 * 64 * 4 * i);
+      const char* g0 = g + (uint64_t)(uint32_t)kv0 * (uint32_t)rsb;
+      dma16n<NI>(vo, g0, base);
     } else {
       const int last = p.Skv - 1 - kv0;
 #pragma unroll
@@ -259,16 +285,16 @@ void fwd_kernel(FwdParams p) {
   // masked pass reads them from global memory).
   const int* doc_row = nullptr;
   if constexpr (DL) doc_row = p.mask.doc + (long long)b * p.mask.doc_stride_b;
-  auto issue_k = [&](int j) {
-    issue_one(Kp, ksb, k_lds[j % NK], kchunk, k_voff, kv0_of(j));
+  auto issue_k = [&](int j, int jm) {
+    issue_one(Kp, ksb, k_lds[jm % NK], kchunk, k_vo, kv0_of(j));
     if constexpr (DL) {
       const int kv0 = kv0_of(j);
       if (p.mask.doc_vec && wave == 0 && kv0 + HB <= p.Skv) {
-        if (lane < HB / 4) dma16(doc_row + kv0 + 4 * lane, lds_address(doc_lds[j % 3]));
+        if (lane < HB / 4) dma16(doc_row + kv0 + 4 * lane, lds_address(doc_lds[jm % 3]));
       }
     }
   };
-  auto issue_v = [&](int j) { issue_one(Vp, vsb, v_lds[j % NV], vchunk, v_voff, kv0_of(j)); };
+  auto issue_v = [&](int j, int jm) { issue_one(Vp, vsb, v_lds[jm % NV], vchunk, v_vo, kv0_of(j)); };
   // Bias tile of sub-tile j -> b_lds[j % 2]: wave w issues slots 64 (4w + i) + lane
   // (i < 4), i.e. row 32 w + 8 i + lane / 8, stored slot lane % 8 holding chunk
   // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ (lane / 16) ^ (4 (i % 2)).
@@ -284,10 +310,10 @@ void fwd_kernel(FwdParams p) {
     b_voff1 = (uint32_t)(b_row * bsb + 16 * (bc0 ^ 4));
   }
   constexpr int NB = 4;  // bias loads per wave per sub-tile
-  auto issue_b = [&](int j) {
+  auto issue_b = [&](int j, int jm) {
     if constexpr (BL) {
       const int kv0 = kv0_of(j);
-      const uint32_t base = lds_address(b_lds[j % 2]) + 16 * 64 * 4 * wave;
+      const uint32_t base = lds_address(b_lds[jm % 2]) + 16 * 64 * 4 * wave;
       const int r0 = q0 + 32 * wave;  // first row of the wave
       if (r0 + 32 <= p.Sq && kv0 + HB <= p.Skv) {
         const char* g0 = Bbh + (long long)r0 * bsb + 2 * kv0;
@@ -388,11 +414,11 @@ void fwd_kernel(FwdParams p) {
   };
 
   // Software pipeline (per wave), step j:
-  //   B: score_mod / mask / row max of sub-tile j     interleaved with  O += PV of sub-tile j-1
+  //   (phased: O += PV of sub-tile j-1 and S = QK^T of sub-tile j+1, MFMAs only)
+  //   B: score_mod / mask / row max of sub-tile j     (interleaved: with O += PV of j-1)
   //   C: (rare) raise the reference max: rescale O (which now includes j-1) and the scores
-  //   D: P = exp2(scores) of sub-tile j, row sums     interleaved with  S = QK^T of sub-tile j+1
-  // so every stretch of VALU work has independent MFMAs of the same wave beside
-  // it.  Loads run ahead: K of j+2 and V of j+1 are issued at the start of step j.
+  //   D: P = exp2(scores) of sub-tile j, row sums     (interleaved: with S = QK^T of j+1)
+  // Loads run ahead: K of j+2 and V of j+1 are issued at the start of step j.
   const int J = SPT * T;
   if (J > 0) {
     // V stage 2 stands in for "sub-tile -1" (P = 0) at step 0: clear it
@@ -404,11 +430,11 @@ void fwd_kernel(FwdParams p) {
     // the wave has read its rows of that stage); in the issue order it sits
     // after K(j) and V(j-1).
     constexpr int NBI = BL ? NB : 0;
-    issue_k(0);
-    issue_b(0);
-    if (J > 1) issue_k(1);
-    issue_v(0);
-    if (J > 1) issue_b(1);
+    issue_k(0, 0);
+    issue_b(0, 0);
+    if (J > 1) issue_k(1, 1);
+    issue_v(0, 0);
+    if (J > 1) issue_b(1, 1);
     if (J > 1)
       wait_vmcnt<2 * NI + NBI>();  // K(0) and the bias of 0 landed (K(1), V(0), bias of 1 may be in flight)
     else
@@ -425,8 +451,12 @@ void fwd_kernel(FwdParams p) {
 
     f32x16_t (&s_cur)[2] = s_a;
     f32x16_t (&s_nxt)[2] = s_b;
-    for (int j = 0; j < J; ++j) {
-      const int H = j % SPT;
+    // The loop is unrolled by 6 (the least common multiple of the ring depths), so
+    // every LDS stage is a compile-time constant: operand reads take it in their
+    // immediate offset and the DMA its M0 value.
+    auto step = [&](const int j, auto jmc) __attribute__((always_inline)) {
+      constexpr int JM = decltype(jmc)::value;
+      const int H = JM % SPT;
       // K(j+1), V(j-1) and the bias of j landed for every wave (only V(j) and
       // the bias of j+1 may be in flight), and every wave is done with step
       // j-1: K stage j % 2 and V stage (j+1) % 3 are free.
@@ -442,16 +472,41 @@ void fwd_kernel(FwdParams p) {
         win = list_entry(t + lane);
         loaded(win);
       }
-      if (j + 2 < J) issue_k(j + 2);
-      if (j + 1 < J) issue_v(j + 1);
+      if (j + 2 < J) issue_k(j + 2, (JM + 2) % 6);
+      if (j + 1 < J) issue_v(j + 1, (JM + 1) % 6);
 
       const int kvt0 = kb_of(t) * kBN + HB * H;
       const bool partial = t < n_part;
       const bool ragged = kvt0 + HB > p.Skv;
-      set_v_stage(v_lds[(j + NV - 1) % NV]);  // V of j-1
-      set_k_stage(k_lds[(j + 1) % NK]);       // K of j+1 (stale on the last step: result unused)
+      set_v_stage(v_lds[(JM + NV - 1) % NV]);  // V of j-1
+      set_k_stage(k_lds[(JM + 1) % NK]);       // K of j+1 (stale on the last step: result unused)
 
-      // ---- B: scores of j  ||  PV of j-1
+      // ---- phased: PV of j-1 and QK^T of j+1, MFMAs only, at raised priority
+      if constexpr (PH) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < 4 * DT; ++i) pv_mfma(p_prev, i);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) qk_mfma(s_nxt, i);
+        // Instruction order: every MFMA's operands are read PF MFMAs ahead (two
+        // ds_read_b64_tr_b16 for a PV MFMA, one ds_read_b128 for a QK^T MFMA).
+        // Masks: 0x008 MFMA, 0x100 LDS read.
+        constexpr int PF = 4, NPV = 4 * DT, NQK = 2 * KS;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+        for (int i = 0; i < NPV + NQK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          const int r = i + PF;  // the MFMA whose operands are read now
+          if (r < NPV)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          else if (r < NPV + NQK)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the softmax VALU stays after the MFMAs
+        __builtin_amdgcn_s_setprio(0);
+      }
+
+      // ---- B: scores of j  (interleaved: || PV of j-1)
       // Element (mt, r) of this lane holds key kvb + cr, cr = 32 mt + 8 (r/4) + r%4.
       const int kvb = kvt0 + 4 * hh;
       const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
@@ -462,7 +517,7 @@ void fwd_kernel(FwdParams p) {
       uint32_t bias2[8][2];
       if constexpr (BL) {
         const int br = 32 * wave + lq;
-        const uint32_t rowa = lds_address(b_lds[j % 2]) + 128 * br + 8 * hh;
+        const uint32_t rowa = lds_address(b_lds[JM % 2]) + 128 * br + 8 * hh;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
           const uint64_t w =
@@ -474,7 +529,7 @@ void fwd_kernel(FwdParams p) {
         // step: nothing else to wait for), its stage takes the tile of j+2
         if (j + 2 < J) {
           wait_lds_reads();
-          issue_b(j + 2);
+          issue_b(j + 2, (JM + 2) % 6);
         }
       }
 #pragma unroll
@@ -493,7 +548,9 @@ void fwd_kernel(FwdParams p) {
         }
         s_cur[mt][r] = y;
         if constexpr (!Score::kBounded) ymax = fmaxf(ymax, y);
-        if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
+        if constexpr (!PH) {
+          if ((e & 1) && (e >> 1) < 4 * DT) pv_mfma(p_prev, e >> 1);
+        }
       }
       // Keep the row max of the unmasked scores here, beside the PV MFMAs: left
       // alone, the compiler moves it (and a copy of every score register) past
@@ -515,7 +572,7 @@ void fwd_kernel(FwdParams p) {
           // once (a whole tile here, so only the mask decides; a partial tile,
           // since the tile is not ragged).
           typedef int i32x4_t __attribute__((ext_vector_type(4)));
-          const uint32_t ids0 = lds_address(doc_lds[DL ? j % 3 : 0]) + 16 * hh;  // keys kvb = kvt0 + 4 hh
+          const uint32_t ids0 = lds_address(doc_lds[DL ? JM % 3 : 0]) + 16 * hh;  // keys kvb = kvt0 + 4 hh
           i32x4_t v[8];
 #pragma unroll
           for (int g = 0; g < 8; ++g)  // keys kvb + 32 (g / 4) + 8 (g % 4) + {0..3}
@@ -569,8 +626,11 @@ void fwd_kernel(FwdParams p) {
           }
         }
       }
+
+      if constexpr (!PH) {
 #pragma unroll
-      for (int i = 16; i < 4 * DT; ++i) pv_mfma(p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
+        for (int i = 16; i < 4 * DT; ++i) pv_mfma(p_prev, i);  // (D=128 has 16 PV MFMAs: none left)
+      }
 
       // ---- C: raise the reference max when needed (never for a bounded score)
       if constexpr (!Score::kBounded) ymax = max_across_halves(ymax);
@@ -588,7 +648,7 @@ void fwd_kernel(FwdParams p) {
         m_run = m_new;
       }
 
-      // ---- D: P of j  ||  S of j+1
+      // ---- D: P of j  (interleaved: || S of j+1)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {  // 16-key k-step g of the PV product
         const int mt = g >> 1, h8 = 8 * (g & 1);
@@ -600,16 +660,34 @@ void fwd_kernel(FwdParams p) {
           pk[k][0] = (__bf16)e0;
           pk[k][1] = (__bf16)e1;
           l_run[k] += e0 + e1;
-          if (4 * g + k < 2 * KS) qk_mfma(s_nxt, 4 * g + k);  // D=64 has 8 QK MFMAs
+          if constexpr (!PH) {
+            if (4 * g + k < 2 * KS) qk_mfma(s_nxt, 4 * g + k);  // D=64 has 8 QK MFMAs
+          }
         }
         p_prev[g] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                             __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
                                             0, 1, 2, 3, 4, 5, 6, 7);
       }
+      if constexpr (!PH) {
 #pragma unroll
-      for (int i = 16; i < 2 * KS; ++i) qk_mfma(s_nxt, i);  // (D=128 has 16 QK MFMAs: none left)
+        for (int i = 16; i < 2 * KS; ++i) qk_mfma(s_nxt, i);  // (D=128 has 16 QK MFMAs: none left)
+      }
       s_cur[0] = s_nxt[0];
       s_cur[1] = s_nxt[1];
+    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    typedef std::integral_constant<int, 2> I2;
+    typedef std::integral_constant<int, 3> I3;
+    typedef std::integral_constant<int, 4> I4;
+    typedef std::integral_constant<int, 5> I5;
+    for (int j = 0; j < J; j += 6) {
+      step(j, I0{});
+      if (j + 1 < J) step(j + 1, I1{});
+      if (j + 2 < J) step(j + 2, I2{});
+      if (j + 3 < J) step(j + 3, I3{});
+      if (j + 4 < J) step(j + 4, I4{});
+      if (j + 5 < J) step(j + 5, I5{});
     }
     // PV of the last sub-tile
     wait_vmcnt<0>();

@@ -141,7 +141,7 @@ typedef struct {
 /* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]
  * (for decode: the KV cache, Skv = its capacity).  Strides are in elements
  * for dims (b, h, s, d); the d stride must be 1, other strides multiples of 8,
- * base pointers 16-byte aligned.  GQA: query head hq reads KV head
+ * the K/V row (s) strides below 2^25, base pointers 16-byte aligned.  GQA: query head hq reads KV head
  * hq / (Hq / Hkv) (paper review §3.3 lists GQA support). */
 typedef struct {
   const uint16_t* q;
@@ -223,7 +223,7 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE (sizes, Hq % Hkv, strides, BlockMask dims,
  * Bm/Hm not in {1,B}/{1,Hq}, a batch-dependent mask with Bm = 1 < B, a BlockMask
  * built for other lengths), FA_ERR_UNSUPPORTED (D, alignment, kinds, bias
- * stride[3] != 1, a page table), FA_ERR_HIP. */
+ * stride[3] != 1, a K/V row stride of 2^25 or more, a page table), FA_ERR_HIP. */
 fa_status fa_forward(const fa_attn_args* a, void* stream);
 
 /* Host only.  Bytes of decode workspace fa_decode needs for these arguments

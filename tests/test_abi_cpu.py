@@ -92,6 +92,13 @@ def test_forward_validation_codes():
     a = _args(); a.scale = 1e-30  # too small for the preloaded key-offset term
     assert _status(a) == fa.FA_ERR_SHAPE
     assert "scale" in fa.lib().fa_last_error().decode()
+    # K/V rows are addressed with 32-bit offsets inside a 64-key sub-tile
+    for name in ("k_stride", "v_stride"):
+        a = _args(); getattr(a, name)[2] = 1 << 25
+        assert _status(a) == fa.FA_ERR_UNSUPPORTED
+        assert "row stride" in fa.lib().fa_last_error().decode()
+        a = _args(); getattr(a, name)[2] = (1 << 25) - 8
+        assert _status(a) != fa.FA_ERR_UNSUPPORTED
 
 
 def _bm(Bm=1, Hm=1, NQ=2, NK=2, kind=fa.MASK_CAUSAL, Sq=256, Skv=256):
