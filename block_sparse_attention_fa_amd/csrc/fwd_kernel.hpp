@@ -702,6 +702,13 @@ void fwd_kernel(FwdParams p) {
   const float lh = (l_run[0] + l_run[1]) + (l_run[2] + l_run[3]);
   const float l = lh + __shfl_xor(lh, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  {
+  // The lane's row again, from the lane id (mbcnt) and uniform values, so that
+  // no per-lane index stays live across the loop for the output address.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int hh = lane_e >> 5;
+  const int myq = q0 + wave * 32 + (lane_e & 31);
+  const bool q_ok = myq < p.Sq;
   if (q_ok) {
     uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)myq * p.os[2];
 #pragma unroll
@@ -721,6 +728,7 @@ void fwd_kernel(FwdParams p) {
       p.lse[((long long)b * p.Hq + hq) * p.Sq + myq] =
           l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
     }
+  }
   }
 }
 
