@@ -203,6 +203,19 @@ void fwd_kernel(FwdParams p) {
   const int hkv = hq / p.G;
   const int q0 = qb * kBM;
 
+  // ---- per-lane query row (its loads first: they overlap the list loads) ----
+  const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1];
+  const int myq = q0 + wave * 32 + lq;
+  const bool q_ok = myq < p.Sq;
+  const int qc = q_ok ? myq : p.Sq - 1;  // clamped index for mask/score row state
+  bf16x8_t qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (q_ok) raw = *(const u32x4_t*)(Qp + (long long)myq * p.qs[2] + 16 * s + 8 * hh);
+    qreg[s] = __builtin_bit_cast(bf16x8_t, raw);
+  }
+
   // ---- this tile's block lists ----------------------------------------------
   const BlockMaskView& bm = p.bm;
   int n_part, n_full;
@@ -233,12 +246,21 @@ void fwd_kernel(FwdParams p) {
   // A window of 64 list entries lives in one register (lane i: entry win0 + i)
   // and is read back with readlane, so the per-step block lookups touch no
   // memory and never wait on the tile loads in flight.
+  // The first window is loaded without waiting for the counts: both lists'
+  // first 64 entries (in bounds: lanes past NK read entry NK-1), then lane e
+  // takes partial entry e or full entry e - n_part (moved across lanes).
   int win0 = 0;
-  int win = list_entry(lane);
+  int win;
+  {
+    const int lc = min(lane, bm.NK - 1);
+    const int pw = (!bm.dense) ? part_idx[lc] : 0;
+    const int fw = (!bm.dense && bm.separate_full) ? full_idx[lc] : 0;
+    const int fs = __shfl(fw, lane - n_part);  // full entry lane - n_part (lanes >= n_part use it)
+    win = lane >= T ? 0 : lane < n_part ? pw : (bm.dense ? lane - n_part : fs);
+  }
   loaded(win);
   auto kb_of = [&](int t) -> int { return __builtin_amdgcn_readlane(win, t - win0); };
 
-  const uint16_t* Qp = p.q + (long long)b * p.qs[0] + (long long)hq * p.qs[1];
   const char* Kp = (const char*)(p.k + (long long)b * p.ks[0] + (long long)hkv * p.ks[1]);
   const char* Vp = (const char*)(p.v + (long long)b * p.vs[0] + (long long)hkv * p.vs[1]);
   const long long ksb = 2 * p.ks[2], vsb = 2 * p.vs[2];  // row strides in bytes
@@ -332,17 +354,6 @@ void fwd_kernel(FwdParams p) {
   auto k_off = [](int r, int chunk) { return r * D + ((chunk ^ k_swizzle<D>(r)) * 8); };
   auto v_off = [](int r, int chunk) { return r * D + ((chunk ^ v_swizzle<D>(r)) * 8); };
 
-  // ---- per-lane query row ---------------------------------------------------
-  const int myq = q0 + wave * 32 + lq;
-  const bool q_ok = myq < p.Sq;
-  const int qc = q_ok ? myq : p.Sq - 1;  // clamped index for mask/score row state
-  bf16x8_t qreg[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4_t raw = {0u, 0u, 0u, 0u};
-    if (q_ok) raw = *(const u32x4_t*)(Qp + (long long)myq * p.qs[2] + 16 * s + 8 * hh);
-    qreg[s] = __builtin_bit_cast(bf16x8_t, raw);
-  }
   const auto mrow = Mask::row(p.mask, b, hq, qc);
   const auto srow = Score::row(p.score, b, hq, qc);
   // Starting value of every QK^T accumulation: zero, or the score's key-offset
