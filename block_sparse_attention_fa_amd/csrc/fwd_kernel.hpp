@@ -714,32 +714,32 @@ void fwd_kernel(FwdParams p) {
   const float l = lh + __shfl_xor(lh, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   {
-  // The lane's row again, from the lane id (mbcnt) and uniform values, so that
-  // no per-lane index stays live across the loop for the output address.
-  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  const int hh = lane_e >> 5;
-  const int myq = q0 + wave * 32 + (lane_e & 31);
-  const bool q_ok = myq < p.Sq;
-  if (q_ok) {
-    uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)myq * p.os[2];
+    // The lane's row again, from the lane id (mbcnt) and uniform values, so that
+    // no per-lane index stays live across the loop for the output address.
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int hh = lane_e >> 5;
+    const int myq = q0 + wave * 32 + (lane_e & 31);
+    const bool q_ok = myq < p.Sq;
+    if (q_ok) {
+      uint16_t* Op = p.o + (long long)b * p.os[0] + (long long)hq * p.os[1] + (long long)myq * p.os[2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hh;
-        bf16x4_t o4;
-        o4[0] = (__bf16)(oacc[dt][4 * g + 0] * inv);
-        o4[1] = (__bf16)(oacc[dt][4 * g + 1] * inv);
-        o4[2] = (__bf16)(oacc[dt][4 * g + 2] * inv);
-        o4[3] = (__bf16)(oacc[dt][4 * g + 3] * inv);
-        *(bf16x4_t*)(Op + d0) = o4;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * dt + 8 * g + 4 * hh;
+          bf16x4_t o4;
+          o4[0] = (__bf16)(oacc[dt][4 * g + 0] * inv);
+          o4[1] = (__bf16)(oacc[dt][4 * g + 1] * inv);
+          o4[2] = (__bf16)(oacc[dt][4 * g + 2] * inv);
+          o4[3] = (__bf16)(oacc[dt][4 * g + 3] * inv);
+          *(bf16x4_t*)(Op + d0) = o4;
+        }
+      }
+      if (p.lse != nullptr && hh == 0) {
+        p.lse[((long long)b * p.Hq + hq) * p.Sq + myq] =
+            l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
       }
     }
-    if (p.lse != nullptr && hh == 0) {
-      p.lse[((long long)b * p.Hq + hq) * p.Sq + myq] =
-          l > 0.0f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
-    }
-  }
   }
 }
 
