@@ -327,17 +327,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
 // ---- bwd_dkdv ------------------------------------------------------------------------
 // One 512-thread workgroup (8 waves, two per SIMD) per (b, hkv, 128-key tile).
-// Wave w and wave w + 4 own the same 32 keys (a lane per key) and split the
-// work of every 64-row query sub-step j in two halves around a barrier:
-//  * P role (waves 0-3): S = Q K^T, P = exp2(S' - LSE) with the mask and the
-//    rows past Sq zeroed, P mod'(S) to LDS (bf16); after the barrier
-//    dV^T += dO^T P.
-//  * dS role (waves 4-7): dP = dO V^T beside dK^T += Q^T dS of sub-step
-//    j - 1; after the barrier dS = P mod'(S) (dP - Delta) from the P role's
-//    copy, kept (bf16) for the next sub-step.
-// Each role holds one of K / V and one of the dK / dV accumulators, so both fit
-// in the registers of two waves per SIMD; the element-wise work of one wave of
-// a SIMD (P before the barrier, dS after it) runs beside the other's MFMAs.
+// Wave w and wave w + 4 (the same SIMD) own the same 32 keys (a lane per key)
+// and split the work of every 64-row query sub-step j, one barrier per sub-step:
+//  * P role (waves 0-3): S = Q K^T of j beside dV^T += dO^T P of j - 1 (MFMAs),
+//    then P = exp2(S' - LSE) of j with the mask and the rows past Sq zeroed,
+//    P mod'(S) to LDS (bf16) and P kept (bf16) for the next sub-step (VALU).
+//  * dS role (waves 4-7): dS = P mod'(S) (dP - Delta) of j - 1 from the P
+//    role's copy (VALU), then dK^T += Q^T dS of j - 1 beside dP = dO V^T of j
+//    (MFMAs); it also issues every tile load, since its sub-step starts with
+//    element-wise work, not with MFMAs waiting for their operands.
+// The two orders are complementary: the P role's MFMAs run beside the dS
+// role's element-wise work, and the other way round.  Each role holds one of
+// K / V and one of the dK / dV accumulators, so both fit in the registers of
+// two waves per SIMD.
 constexpr int kDkdvThreads = 512;
 
 template <int D, class Mask, class Score>
@@ -357,9 +359,9 @@ void bwd_dkdv_kernel(BwdParams P) {
   __shared__ __align__(16) uint16_t g_lds[3][HB * D];
   // base-2 LSE (first HB floats) and Delta (next HB) of the sub-tile's query rows
   __shared__ __align__(16) float ld_lds[3][2 * HB];
-  // P mod'(S) of the sub-step for the dS role: per wave, four groups of 64
-  // lanes x 16 bytes (elements 8 g .. 8 g + 7 of the lane)
-  __shared__ __align__(16) uint16_t p_lds[4][64 * 32];
+  // P mod'(S) of sub-step j for the dS role, in buffer j % 2: per wave, four
+  // groups of 64 lanes x 16 bytes (elements 8 g .. 8 g + 7 of the lane)
+  __shared__ __align__(16) uint16_t p_lds[2][4][64 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,13 +436,13 @@ void bwd_dkdv_kernel(BwdParams P) {
     ch = 0;
   };
 
-  // Loads: the P-role waves bring the Q sub-tile, the dS-role waves the dO
-  // sub-tile (each 4 waves x NI loads), wave 0 the LSE / Delta rows.
+  // Loads: the dS-role waves bring the Q and dO sub-tiles (each 4 waves x NI
+  // loads), wave 4 the LSE / Delta rows.
   constexpr int RPI = 64 / CPR;
   const int lrow = kw * RPI + lane / CPR;
   const int kchunk = (lane % CPR) ^ rt_swizzle<D>(lrow);
-  const long long xsb = ds_role ? 2 * P.dos[2] : 2 * p.qs[2];
-  const uint32_t x_voff = (uint32_t)(lrow * xsb + 16 * kchunk);
+  const long long gsb = 2 * P.dos[2], qsb = 2 * p.qs[2];
+  const uint32_t g_voff = (uint32_t)(lrow * gsb + 16 * kchunk), q_voff = (uint32_t)(lrow * qsb + 16 * kchunk);
   auto issue_one = [&](const char* g, long long rsb, const uint16_t* buf, uint32_t voff, int r0) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(buf) + 16 * 64 * kw);
     if (r0 + HB <= p.Sq) {
@@ -476,12 +478,11 @@ void bwd_dkdv_kernel(BwdParams P) {
     const int r0 = s.qs0;
     if (ds_role) {
       const char* Gh = (const char*)(P.dout + (long long)b * P.dos[0] + (long long)s.hq * P.dos[1]);
-      issue_one(Gh, xsb, g_lds[j % 3], x_voff, r0);
-    } else {
       const char* Qh = (const char*)(p.q + (long long)b * p.qs[0] + (long long)s.hq * p.qs[1]);
-      issue_one(Qh, xsb, q_lds[j % 3], x_voff, r0);
+      issue_one(Qh, qsb, q_lds[j % 3], q_voff, r0);
+      issue_one(Gh, gsb, g_lds[j % 3], g_voff, r0);
     }
-    if (wave == 0 && lane < 2 * HB / 4) {  // 16 bytes a lane; the workspace rows are padded
+    if (wave == 4 && lane < 2 * HB / 4) {  // 16 bytes a lane; the workspace rows are padded
       const long long w0 = ((long long)b * p.Hq + s.hq) * P.sq_pad + r0 + 4 * (lane % (HB / 4));
       dma16((lane < HB / 4 ? P.ws_lse2 : P.ws_delta) + w0, lds_address(ld_lds[j % 3]));
     }
@@ -505,8 +506,9 @@ void bwd_dkdv_kernel(BwdParams P) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // this lane's four 16-byte groups in the P mod'(S) buffer
-  const uint32_t pbase = lds_address(p_lds[kw]) + 16 * lane;
-  auto p_addr = [&](int g) { return pbase + 1024 * g; };
+  const uint32_t pbase = lds_address(p_lds[0][kw]) + 16 * lane;
+  constexpr uint32_t kPBuf = 4 * 64 * 32 * 2;  // bytes between the two buffers
+  auto p_addr = [&](int j, int g) { return pbase + ((j & 1) ? kPBuf : 0u) + 1024 * g; };
 
   f32x16_t acc[DT];  // dV (P role) or dK (dS role)
 #pragma unroll
@@ -521,9 +523,45 @@ void bwd_dkdv_kernel(BwdParams P) {
     acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[i & 1], dsb[i / DT], acc[i % DT], 0, 0, 0);
   };
 
-  // One sub-step; the ring stage j % 3 is a compile-time constant (the loop
-  // below is unrolled by 3) so that every LDS read address is a per-lane
-  // register plus an immediate offset.  Sub-step descriptors run two ahead.
+  // dV^T += dO^T P for a sub-step whose dO is at gb, P (bf16) in bo; MFMA i is
+  // k-step i / DT (16 query rows), d block i % DT
+  bf16x8_t bo[4];  // (P role) P of the last sub-step, bf16 B operands
+  auto dv_mfma = [&](uint32_t gb, int i, bf16x8_t (&tg)[2]) {
+    if (i + 1 < 4 * DT) tg[(i + 1) & 1] = tr_read(gb, (i + 1) % DT, (i + 1) / DT);
+    acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tg[i & 1], bo[i / DT], acc[i % DT], 0, 0, 0);
+  };
+  // dS role: dS = P mod'(S) (dP - Delta) of sub-step jj as bf16 B operands (k =
+  // query row; k-step g holds elements 8 g .. 8 g + 7), from the P role's copy in
+  // LDS, dP in sd and Delta at ldp
+  f32x16_t sd[2] = {f32x16_t{}, f32x16_t{}};  // S then P (P role), dP (dS role)
+  auto make_ds = [&](int jj, uint32_t ldp) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int mt = g >> 1, h8 = 8 * (g & 1);
+      const u32x4_t pm = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(jj, g);
+      // elements h8 .. h8 + 7 are rows 2 h8 + {0..3} and 2 h8 + 8 + {0..3} of the block (+ 4 hh)
+      const f32x4_t d0 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8));
+      const f32x4_t d1 =
+          *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8 + 8));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t w = pm[k >> 1];
+        const float pv = bf16_bits_to_float((k & 1) ? (w >> 16) : (w & 0xffffu));
+        const float dl = (k < 4) ? d0[k] : d1[k - 4];
+        dsb[g][k] = (__bf16)(pv * (sd[mt][h8 + k] - dl));
+      }
+    }
+  };
+
+  // One sub-step j, one barrier.  The two waves of a SIMD run complementary
+  // orders, so that each one's MFMAs run beside the other's element-wise work:
+  //  * P role: S = Q K^T of j and dV^T += dO^T P of j - 1 (MFMAs), then P of j
+  //    and P mod'(S) to LDS buffer j % 2 (VALU), P kept as bf16 for step j + 1;
+  //  * dS role: dS of j - 1 from LDS buffer (j - 1) % 2 (VALU), then
+  //    dK^T += Q^T dS of j - 1 and dP = dO V^T of j (MFMAs).
+  // The ring stage j % 3 is a compile-time constant (the loop below is unrolled
+  // by 3) so that every LDS read address is a per-lane register plus an
+  // immediate offset.  Sub-step descriptors run two ahead.
   Sub nxt{0, 0, false}, nx2{0, 0, false};
   // (the role is a compile-time constant of each copy, so the two roles'
   // registers are allocated apart; both pass the same barriers)
@@ -531,8 +569,11 @@ void bwd_dkdv_kernel(BwdParams P) {
     constexpr int st = decltype(stage)::value, sp = (st + 2) % 3;
     constexpr bool ds_role = decltype(role)::value;
     wait_vmcnt<0>();
-    wait_lds_reads();
-    __syncthreads();  // sub-step j landed; every wave is done with j - 2, whose stage j + 1 reuses
+    wait_lds_reads();  // (lgkmcnt covers the LDS writes too)
+    // sub-step j landed and P mod'(S) of j - 1 is in LDS; every wave is done
+    // with step j - 1, so stage j + 1 (last used for j - 2) and P buffer j % 2
+    // (last read for j - 2) are free
+    __syncthreads();
     const Sub cur = nxt;
     nxt = nx2;
     if (j + 1 < Jtot) issue(nxt, j + 1);
@@ -540,36 +581,42 @@ void bwd_dkdv_kernel(BwdParams P) {
     const uint32_t gbase = lds_address(g_lds[st]);
     const uint32_t qbase = lds_address(q_lds[st]);
     constexpr int PF = 4;  // A-operand reads run PF MFMAs ahead
-    // S = Q K^T (P role) or dP = dO V^T (dS role): MFMA i is query block i % 2,
-    // k-step i / 2 (two accumulation chains)
+    // S = Q K^T (P role) or dP = dO V^T (dS role) of j: MFMA i is query block
+    // i % 2, k-step i / 2 (two accumulation chains)
     const uint32_t abase = ds_role ? gbase : qbase;
     auto rd_a = [&](int i) {
       return *(const lds_bf16x8_t*)(uintptr_t)(abase + 2 * (aoff[i >> 1] + (i & 1) * 32 * D));
     };
-    // (dS role, j > 0) one dK MFMA of sub-step j - 1 after each
-    f32x16_t sd[2] = {f32x16_t{}, f32x16_t{}};
+    if constexpr (ds_role) {
+      if (j > 0) make_ds(j - 1, lds_address(ld_lds[sp]) + 16 * hh + 4 * HB);
+    }
     {
-      static_assert(2 * KS == 4 * DT, "dP and dK MFMAs pair up");
-      const bool with_dk = ds_role && j > 0;  // (false at compile time for the P role)
-      const uint32_t qprev = lds_address(q_lds[sp]);
+      static_assert(2 * KS == 4 * DT, "S/dP and dV/dK MFMAs pair up");
+      // the MFMAs of j - 1: dV (P role, operand dO^T of j - 1) or dK (dS role, Q^T of j - 1)
+      const bool with_prev = j > 0;
+      // (stage sp of the ring as an offset from stage st: both are compile-time)
+      const uint32_t pb = ds_role ? qbase + (uint32_t)(sp - st) * (uint32_t)sizeof(q_lds[0])
+                                  : gbase + (uint32_t)(sp - st) * (uint32_t)sizeof(g_lds[0]);
       bf16x8_t aq[2 * KS], tq[2];
 #pragma unroll
       for (int i = 0; i < PF; ++i) aq[i] = rd_a(i);
-      // The P role runs at a raised wave priority through its first half: its
-      // S MFMAs then go first on the SIMD, and its element-wise pass (the
-      // longer of the two halves' critical paths) runs beside the dS role's
-      // dP and dK MFMAs.  (-4% time against equal priorities.)
-      if constexpr (!ds_role) __builtin_amdgcn_s_setprio(2);
-      if (with_dk) tq[0] = tr_read(qprev, 0, 0);
+      if (with_prev) tq[0] = tr_read(pb, 0, 0);
+      sd[0] = f32x16_t{};
+      sd[1] = f32x16_t{};
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {
         if (i + PF < 2 * KS) aq[i + PF] = rd_a(i + PF);
         sd[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[i], xreg[i >> 1], sd[i & 1], 0, 0, 0);
-        if (with_dk) dk_mfma(qprev, i, tq);
+        if (with_prev) {
+          if constexpr (ds_role)
+            dk_mfma(pb, i, tq);
+          else
+            dv_mfma(pb, i, tq);
+        }
       }
     }
     if constexpr (!ds_role) {
-      // ---- P role: P, P mod'(S) to LDS ----
+      // ---- P role: P of j, P mod'(S) to LDS, P as bf16 for step j + 1 ----
       const int hq = cur.hq, qs0 = cur.qs0;  // query head, first query row of the sub-step
       const bool partial = cur.partial;
       const auto scol = Score::col(p.score, Score::row(p.score, b, hq, 0), qs0 + 4 * hh, kvc);
@@ -609,51 +656,11 @@ void bwd_dkdv_kernel(BwdParams P) {
         const int mt = g >> 1, h8 = 8 * (g & 1);
         bf16x8_t pmb;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pmb[k] = (__bf16)pm[mt][h8 + k];
-        *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(g) = __builtin_bit_cast(u32x4_t, pmb);
-      }
-    }
-    if constexpr (!ds_role) __builtin_amdgcn_s_setprio(0);  // (back to the dS role's)
-    wait_lds_reads();  // (lgkmcnt covers the LDS writes too)
-    __syncthreads();  // P mod'(S) of sub-step j is in LDS
-    if constexpr (!ds_role) {
-      // second half: dV^T += dO^T P; MFMA i is k-step i / DT (16 query rows),
-      // d block i % DT, its A operand (a transposed read) PFT MFMAs ahead
-      bf16x8_t bo[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int mt = g >> 1, h8 = 8 * (g & 1);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bo[g][k] = (__bf16)sd[mt][h8 + k];
-      }
-      constexpr int NM = 4 * DT, PFT = 4;
-      bf16x8_t tro[NM];
-#pragma unroll
-      for (int i = 0; i < PFT; ++i) tro[i] = tr_read(gbase, i % DT, i / DT);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        if (i + PFT < NM) tro[i + PFT] = tr_read(gbase, (i + PFT) % DT, (i + PFT) / DT);
-        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tro[i], bo[i / DT], acc[i % DT], 0, 0, 0);
-      }
-    } else {
-      // second half: dS = P mod'(S) (dP - Delta) as bf16 B operands (k =
-      // query row): k-step g holds elements 8 g .. 8 g + 7
-      const uint32_t ldp = lds_address(ld_lds[st]) + 16 * hh + 4 * HB;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int mt = g >> 1, h8 = 8 * (g & 1);
-        const u32x4_t pm = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(g);
-        // elements h8 .. h8 + 7 are rows 2 h8 + {0..3} and 2 h8 + 8 + {0..3} of the block (+ 4 hh)
-        const f32x4_t d0 = *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8));
-        const f32x4_t d1 =
-            *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)(ldp + 4 * (32 * mt + 2 * h8 + 8));
-#pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t w = pm[k >> 1];
-          const float pv = bf16_bits_to_float((k & 1) ? (w >> 16) : (w & 0xffffu));
-          const float dl = (k < 4) ? d0[k] : d1[k - 4];
-          dsb[g][k] = (__bf16)(pv * (sd[mt][h8 + k] - dl));
+          pmb[k] = (__bf16)pm[mt][h8 + k];
+          bo[g][k] = (__bf16)sd[mt][h8 + k];
         }
+        *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)p_addr(j, g) = __builtin_bit_cast(u32x4_t, pmb);
       }
     }
   };
@@ -673,12 +680,23 @@ void bwd_dkdv_kernel(BwdParams P) {
     run(std::true_type{});
   else
     run(std::false_type{});
-  if (Jtot > 0 && ds_role) {  // dK of the last sub-step (its Q stage is still intact)
-    const uint32_t ql = lds_address(q_lds[(Jtot - 1) % 3]);
+  if (Jtot > 0) {  // the MFMAs of the last sub-step (its stages are still intact)
+    wait_lds_reads();
+    __syncthreads();  // P mod'(S) of the last sub-step is in LDS
+    const int jl = Jtot - 1, sl = jl % 3;
     bf16x8_t tq[2];
-    tq[0] = tr_read(ql, 0, 0);
+    if (ds_role) {
+      make_ds(jl, lds_address(ld_lds[0]) + sl * (uint32_t)sizeof(ld_lds[0]) + 16 * hh + 4 * HB);
+      const uint32_t ql = lds_address(q_lds[0]) + sl * (uint32_t)sizeof(q_lds[0]);
+      tq[0] = tr_read(ql, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) dk_mfma(ql, i, tq);
+      for (int i = 0; i < 4 * DT; ++i) dk_mfma(ql, i, tq);
+    } else {
+      const uint32_t gl = lds_address(g_lds[0]) + sl * (uint32_t)sizeof(g_lds[0]);
+      tq[0] = tr_read(gl, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DT; ++i) dv_mfma(gl, i, tq);
+    }
   }
 
   if (kv_ok) {  // dV from the P role, dK (times the scale) from the dS role
