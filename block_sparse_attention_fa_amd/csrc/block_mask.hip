@@ -163,6 +163,49 @@ __global__ __launch_bounds__(64) void transpose_block_lists_kernel(BuildParams p
   }
 }
 
+// Work order of the query blocks (the BlockMask's optional q_order): one
+// 1024-thread workgroup per (b', h') row sorts the keys (weight << 14) | qb in
+// LDS with a bitonic network, largest first, and writes their qb.  weight =
+// 3 per listed tile that runs the mask_mod + 2 per full tile, at most 3 NK <
+// 2^16, and qb < 2^14, so the keys are distinct and fit 30 bits.  Slots past
+// NQ hold 0, which sorts after every real key except (weight 0, qb 0), whose
+// decoded qb is the same.
+constexpr int kOrderMax = 16384;
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void order_query_blocks_kernel(BuildParams p) {
+  __shared__ uint32_t key[kOrderMax];
+  const long long bh = (long long)blockIdx.y * p.Hm + blockIdx.x;
+  int n = 2;
+  while (n < p.NQ) n <<= 1;
+  for (int i = threadIdx.x; i < n; i += kOrderThreads) {
+    uint32_t k = 0;
+    if (i < p.NQ) {
+      const long long row = bh * p.NQ + i;
+      const int w = 3 * p.kv_num[row] + (p.separate_full ? 2 * p.full_num[row] : 0);
+      k = ((uint32_t)w << 14) | (uint32_t)i;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kOrderThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = key[i], b = key[l];
+          const bool desc = (i & k) == 0;  // this pair's subsequence runs largest first
+          if (desc ? a < b : a > b) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < p.NQ; i += kOrderThreads) p.q_order[bh * p.NQ + i] = (int)(key[i] & 0x3fffu);
+}
+
 struct LaunchBuild {
   const BuildParams& p;
   hipStream_t stream;
@@ -172,6 +215,8 @@ struct LaunchBuild {
     hipLaunchKernelGGL(build_block_mask_kernel<Mask>, grid, dim3(kThreads), 0, stream, p);
     if (p.q_num != nullptr)
       hipLaunchKernelGGL(transpose_block_lists_kernel, dim3(p.NK, p.Hm, p.Bm), dim3(64), 0, stream, p);
+    if (p.q_order != nullptr)
+      hipLaunchKernelGGL(order_query_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream, p);
   }
 };
 

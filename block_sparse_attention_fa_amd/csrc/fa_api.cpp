@@ -138,6 +138,7 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
     p.bm.NQ = NQ;
     p.bm.Bm = p.bm.Hm = 1;
     p.bm.separate_full = 1;
+    p.bm.q_order = nullptr;
   } else {
     if (bm->block_q != FA_BLOCK || bm->block_kv != FA_BLOCK)
       return fail(FA_ERR_UNSUPPORTED, "BlockMask block size %dx%d (supported: 128x128)", bm->block_q, bm->block_kv);
@@ -163,6 +164,7 @@ fa_status prepare(const fa_attn_args* a, bool decode, FwdParams& p, int& mask_ki
     p.bm.NK = NK;
     p.bm.dense = 0;
     p.bm.separate_full = bm->separate_full;
+    p.bm.q_order = bm->q_order;
     p.mask = mask_params(bm->mask);
     mask_kind = bm->mask.kind;
   }
@@ -368,6 +370,8 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   if (n_transposed != 0 && n_transposed != 4)
     return fail(FA_ERR_NULL, "the transposed view needs all four of q_num_blocks, q_indices, "
                              "full_q_num_blocks and full_q_indices (or none)");
+  if (bm->q_order != nullptr && bm->NQ > 16384)
+    return fail(FA_ERR_UNSUPPORTED, "q_order needs NQ <= 16384 (got %d)", bm->NQ);
   fa_status st = check_mask(bm->mask, Sq, Skv);
   if (st != FA_OK) return st;
 
@@ -380,6 +384,7 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   p.q_idx = bm->q_indices;
   p.full_q_num = bm->full_q_num_blocks;
   p.full_q_idx = bm->full_q_indices;
+  p.q_order = bm->q_order;
   p.Bm = bm->Bm;
   p.Hm = bm->Hm;
   p.NQ = bm->NQ;

@@ -41,6 +41,7 @@ struct BlockMaskView {
   int Bm, Hm, NQ, NK;
   int dense;          // no BlockMask: every kv tile is treated as full
   int separate_full;  // 0: kv_* already holds every non-empty tile
+  const int* q_order; // nullptr, or each row's query blocks heaviest first [Bm,Hm,NQ]
 };
 
 struct FwdParams {
@@ -95,6 +96,7 @@ struct BuildParams {
   int* q_idx;
   int* full_q_num;
   int* full_q_idx;
+  int* q_order;     // work order of the query blocks, nullptr when not requested
   int Bm, Hm, NQ, NK, Sq, Skv;
   int separate_full;
   MaskParams mask;

@@ -194,12 +194,24 @@ void fwd_kernel(FwdParams p) {
 
   // ---- which (b, hq, query tile) ------------------------------------------
   const int NQ = (p.Sq + kBM - 1) / kBM;
-  const int total = NQ * p.Hq * p.B;
-  const int L = xcd_logical_id(blockIdx.x, total);
-  const int i_in_head = L % NQ;
-  const int bh = L / NQ;
+  const int BH = p.Hq * p.B;
+  int bh, qb;
+  if (p.bm.q_order != nullptr && BH % 8 == 0) {
+    // The BlockMask orders each row's query tiles heaviest first.  XCD x
+    // (workgroup id % 8) takes heads x, x + 8, ...; its m-th workgroup is the
+    // (m / heads-per-XCD)-th heaviest tile of one of them, so each XCD starts
+    // the longest units of all its heads first.
+    const int x = blockIdx.x & 7, m = blockIdx.x >> 3, hpx = BH >> 3;
+    const int r = m / hpx;
+    bh = x + 8 * (m - r * hpx);
+    const int mb = p.bm.Bm > 1 ? bh / p.Hq : 0, mh = p.bm.Hm > 1 ? bh % p.Hq : 0;
+    qb = min(max(p.bm.q_order[((long long)mb * p.bm.Hm + mh) * NQ + r], 0), NQ - 1);
+  } else {
+    const int L = xcd_logical_id(blockIdx.x, NQ * BH);
+    bh = L / NQ;
+    qb = NQ - 1 - L % NQ;  // later (heavier, for causal) query tiles first
+  }
   const int hq = bh % p.Hq, b = bh / p.Hq;
-  const int qb = NQ - 1 - i_in_head;  // later (heavier, for causal) query tiles first
   const int hkv = hq / p.G;
   const int q0 = qb * kBM;
 

@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 # --- enums (include/fa.h) ----------------------------------------------------
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 FA_BLOCK = 128
+ABI_VERSION = 4          # the layout of the structs below (include/fa.h FA_ABI_VERSION)
+MAX_ORDER_NQ = 16384     # largest NQ for which fa_build_block_mask can write q_order
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_SLIDING_CAUSAL = 0, 1, 2, 3
 MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL, MASK_PREFIX_LM, MASK_KV_LEN = 4, 5, 6, 7
@@ -53,7 +55,8 @@ class BlockMaskC(ctypes.Structure):
                 ("block_q", c_int32), ("block_kv", c_int32), ("separate_full", c_int32),
                 ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc),
                 ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
-                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p)]
+                ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p),
+                ("q_order", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -118,6 +121,9 @@ def lib():
             f = getattr(l, name)
             f.restype = res
             f.argtypes = args
+        if l.fa_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {l.fa_abi_version()}, this binding needs "
+                              f"{ABI_VERSION}: rebuild it")
         _lib = l
     return _lib
 
@@ -247,7 +253,8 @@ class ScoreMod:
 class BlockMask:
     """Device BlockMask: the four int32 tensors of the Concepts page's "Key attributes"."""
 
-    def __init__(self, mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", transposed=False):
+    def __init__(self, mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", transposed=False,
+                 order=None):
         import torch
         NQ, NK = fa_block_mask_dims(Sq, Skv)
         self.mask = mask
@@ -275,6 +282,17 @@ class BlockMask:
             self.full_q_indices = torch.empty((Bm, Hm, NK, NQ), **z)
             c.q_num_blocks, c.q_indices = self.q_num_blocks.data_ptr(), self.q_indices.data_ptr()
             c.full_q_num_blocks, c.full_q_indices = self.full_q_num_blocks.data_ptr(), self.full_q_indices.data_ptr()
+        # work order of the query blocks (heaviest first), which the forward
+        # follows when it starts its workgroups.  By default only for document
+        # masks, whose work per query tile follows the position inside the
+        # document; the causal, window and prefix masks already have the
+        # heaviest tiles last, which the forward starts first without it.
+        if order is None:
+            order = mask.kind in (MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL)
+        self.q_order = None
+        if order and NQ <= MAX_ORDER_NQ:
+            self.q_order = torch.empty((Bm, Hm, NQ), **z)
+            c.q_order = self.q_order.data_ptr()
 
     def list_every_tile(self):
         """Re-encode as "no block skipping": every tile of every row is listed as
@@ -336,12 +354,14 @@ def fa_block_mask_dims(Sq, Skv, block_q=FA_BLOCK, block_kv=FA_BLOCK):
 
 
 def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, device="cuda", stream=None,
-                        transposed=False):
+                        transposed=False, order=None):
     """Allocate a BlockMask and build it on the device (asynchronously on `stream`);
-    transposed=True also builds the per-KV-block view the backward needs."""
+    transposed=True also builds the per-KV-block view the backward needs, and
+    order=True the heaviest-first work order of the query blocks (q_order;
+    None: for document masks only)."""
     mask.check(Bm, Sq, Skv)
     with _on(stream):
-        bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed)
+        bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed, order)
     _check(lib().fa_build_block_mask(ctypes.byref(bm.c), Sq, Skv, _stream(stream)))
     return bm
 

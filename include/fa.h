@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 #define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
 
 typedef enum {
@@ -136,6 +136,21 @@ typedef struct {
   int32_t* q_indices;
   int32_t* full_q_num_blocks;
   int32_t* full_q_indices;
+  /* Work order of the query blocks (optional; NULL = none): [Bm,Hm,NQ] device
+   * int32 that fa_build_block_mask fills with each row's query blocks sorted
+   * by their work, heaviest first: weight 3 per tile that runs the mask (the
+   * kv_* tiles) plus 2 per tile of full_kv_* (with separate_full = 1), ties
+   * broken by the larger query block; NQ <= 16384.  When it is present and
+   * B*Hq is a multiple of 8, the forward starts its (b, h, query tile) units
+   * in that order, the heaviest tiles of every head of an XCD first (paper
+   * review §4.3: a query tile's work is the length of its lists).  Without it
+   * the forward starts the last query tiles first, which is longest-first for
+   * masks whose work grows with the query index (causal, windows, prefix);
+   * document masks, whose work follows the position inside a document, gain
+   * from the order (about 10% at 16K tokens with ~1.6K-token documents), the
+   * others do not (one more dependent load per workgroup).  The order changes
+   * no result, only which workgroups run together. */
+  int32_t* q_order;
 } fa_block_mask;
 
 /* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]

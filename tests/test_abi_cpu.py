@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 3
+    assert L.fa_abi_version() == 4
     for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                                  "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
         assert L.fa_status_string(code).decode() == name
@@ -218,6 +218,16 @@ def test_transposed_view_is_all_or_nothing():
     c.mask = fa.MaskMod("causal").desc()
     c.q_num_blocks = c.q_indices = 0x20000      # two of the four
     assert fa.lib().fa_build_block_mask(ctypes.byref(c), 256, 256, None) == fa.FA_ERR_NULL
+
+
+def test_q_order_needs_nq_at_most_16384():
+    """The work order of the query blocks is sorted in one workgroup's LDS, so
+    fa_build_block_mask refuses it past 16384 query blocks (before any launch)."""
+    S = 128 * 16385
+    c = _bm(NQ=16385, NK=1, kind=fa.MASK_NONE, Sq=S, Skv=128)
+    c.q_order = 0x30000
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), S, 128, None) == fa.FA_ERR_UNSUPPORTED
+    assert b"16384" in fa.lib().fa_last_error()
 
 
 def _rt_swizzle(D, r):

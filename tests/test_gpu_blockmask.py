@@ -17,7 +17,8 @@ def _check_bitexact(spec, Bm, Hm, Sq, Skv, separate_full=True):
     """Every list, the transposed (per-KV-block) view included, equals the oracle's."""
     from block_sparse_attention_fa_amd import fa
     import torch
-    bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True)
+    bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True,
+                                order=True)
     torch.cuda.synchronize()
     mm = C.oracle_mask(spec) or fo.no_mask()
     ref = fo.block_mask(mm, Bm, Hm, Sq, Skv, separate_full=separate_full)
@@ -25,7 +26,24 @@ def _check_bitexact(spec, Bm, Hm, Sq, Skv, separate_full=True):
         got = getattr(bm, key).cpu().numpy()
         assert got.dtype == np.int32
         np.testing.assert_array_equal(got, ref[key], err_msg=f"{spec['mask']} {key} Sq={Sq} Skv={Skv}")
+    assert bm.q_order is not None
+    np.testing.assert_array_equal(bm.q_order.cpu().numpy(), expected_q_order(ref, separate_full),
+                                  err_msg=f"{spec['mask']} q_order Sq={Sq} Skv={Skv}")
     return bm, ref
+
+
+def expected_q_order(ref, separate_full):
+    """The work order fa_build_block_mask writes (include/fa.h, q_order): each row's
+    query blocks by weight 3 per tile of kv_* + 2 per tile of full_kv_* (the full
+    tiles count only when they are a list of their own), heaviest first, ties
+    by the larger query block; computed here from the oracle's counts."""
+    kn = ref["kv_num_blocks"].astype(np.int64)
+    w = 3 * kn + (2 * ref["full_kv_num_blocks"].astype(np.int64) if separate_full else 0)
+    out = np.empty(w.shape, dtype=np.int32)
+    qb = np.arange(w.shape[-1])
+    for idx in np.ndindex(*w.shape[:-1]):
+        out[idx] = np.lexsort((-qb, -w[idx]))
+    return out
 
 
 @pytest.mark.parametrize("mask", C.MASK_NAMES)

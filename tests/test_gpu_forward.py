@@ -19,11 +19,11 @@ BATCH_DEP = ("document", "document_causal", "kv_len")
 
 
 def run_case(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense=False,
-             per_head_mask=False, with_lse=True, **spec_kw):
+             per_head_mask=False, with_lse=True, order=None, **spec_kw):
     import torch
     from block_sparse_attention_fa_amd import fa
     print(f"[case] seed={seed} mask={mask} score={score} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} "
-          f"sep={separate_full} dense={dense}", flush=True)
+          f"sep={separate_full} dense={dense} order={order}", flush=True)
     q, k, v = gen.qkv(seed, B, Hq, Hkv, Sq, Skv, D)
     spec = C.make_spec(seed, mask, score, B, Hq, Sq, Skv, **spec_kw)
     qt, kt, vt = (gen.to_torch_bf16(x) for x in (q, k, v))
@@ -31,7 +31,7 @@ def run_case(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dens
     if not dense:
         Bm = B if mask in BATCH_DEP else 1
         Hm = Hq if per_head_mask else 1
-        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full)
+        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, order=order)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda") if with_lse else None
     out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=C.gpu_score(spec), lse=lse)
     torch.cuda.synchronize()
@@ -97,6 +97,24 @@ def test_block_lists_longer_than_the_register_window(mask, score, dense, D):
     list entries in one register and slides that window along the row: here 2
     and 4 times."""
     run_case(80 + D, mask, score, 1, 2, 1, 256, 33000, D, dense=dense, prefix=20000)
+
+
+@pytest.mark.parametrize("per_head_mask", [False, True])
+@pytest.mark.parametrize("mask", ["document_causal", "document", "causal", "prefix_lm"])
+def test_work_order_of_query_tiles(mask, per_head_mask):
+    """With the BlockMask's q_order (B*Hq a multiple of 8: each XCD starts the
+    heaviest query tiles of all its heads first) the forward matches the oracle
+    and is bit-identical to the natural order, since the order only moves
+    workgroups.  Ragged tiles, per-batch and per-head BlockMask rows."""
+    got, _ = run_case(50, mask, "alibi", 2, 8, 2, 700, 700, 64, per_head_mask=per_head_mask, order=True)
+    nat, _ = run_case(50, mask, "alibi", 2, 8, 2, 700, 700, 64, per_head_mask=per_head_mask, order=False)
+    assert np.array_equal(got, nat)
+
+
+def test_work_order_with_staged_bias_d128():
+    got, _ = run_case(51, "document_causal", "bias", 1, 8, 8, 520, 520, 128, order=True)
+    nat, _ = run_case(51, "document_causal", "bias", 1, 8, 8, 520, 520, 128, order=False)
+    assert np.array_equal(got, nat)
 
 
 @pytest.mark.parametrize("score", ["none", "alibi", "bias"])
