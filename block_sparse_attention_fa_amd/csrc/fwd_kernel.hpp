@@ -111,6 +111,16 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "m0");
 }
+// The same loads with the non-temporal hint, for data read once (the bias
+// tiles): they then do not push reused K/V tiles out of L2 and MALL.
+__device__ __forceinline__ void dma16_nt(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds)) : "m0");
+}
+__device__ __forceinline__ void dma16s_nt(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)) : "m0");
+}
 // N loads of 16 bytes per lane into LDS at lds + 4096 i + 16 lane (i < N), from
 // sbase + voff[i]: one uniform base and a per-lane offset per load, so a tile's
 // loads cost one scalar address for the tile and an M0 write per load.
@@ -176,7 +186,8 @@ void fwd_kernel(FwdParams p) {
   // bank groups (2-way conflicts where the plain c ^ (r % 8) had 4-way).  Each
   // wave loads and reads only its own 32 rows, so a stage is free again for the
   // wave once it has read it, and the tile of step j+2 goes into the stage of
-  // step j with no barrier.
+  // step j with no barrier.  Every bias element is read once per launch, so its
+  // loads carry the non-temporal hint and leave L2 and MALL to the K/V tiles.
   constexpr bool BL = Score::kStagesBias;
   __shared__ __align__(16) uint16_t b_lds[BL ? 2 : 1][BL ? kBM * HB : 8];
   // Document ids of sub-tiles j, j+1, j+2 (masks that read them, D = 64, where
@@ -352,13 +363,13 @@ void fwd_kernel(FwdParams p) {
       if (r0 + 32 <= p.Sq && kv0 + HB <= p.Skv) {
         const char* g0 = Bbh + (long long)r0 * bsb + 2 * kv0;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) dma16s((i & 1) ? b_voff1 : b_voff0, g0 + 8 * i * bsb, base + 16 * 64 * i);
+        for (int i = 0; i < NB; ++i) dma16s_nt((i & 1) ? b_voff1 : b_voff0, g0 + 8 * i * bsb, base + 16 * 64 * i);
       } else {  // ragged: clamp rows to Sq-1 and chunks to the last one of the row
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int q = min(r0 + 8 * i + b_row, p.Sq - 1);
           const int kc = min(kv0 + 8 * (bc0 ^ (4 * (i & 1))), p.Skv - 8);
-          dma16(Bbh + (long long)q * bsb + 2 * kc, base + 16 * 64 * i);
+          dma16_nt(Bbh + (long long)q * bsb + 2 * kc, base + 16 * 64 * i);
         }
       }
     }
