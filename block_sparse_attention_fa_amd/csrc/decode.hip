@@ -226,7 +226,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     }
   }
   __syncthreads();
-  load_rows(Vp, p.vs[2], true, 0, xa);  // first V rows, in flight during pass 2
+  // the first V rows in flight during pass 2: two groups with a per-sequence
+  // cache (+1%); one with a paged cache, whose kernel would otherwise need
+  // more than 128 registers and lose a wave per SIMD (-10%)
+  constexpr bool V2 = !PAGED;
+  load_rows(Vp, p.vs[2], true, 0, xa);
+  if (V2 && STEP < n_rows) load_rows(Vp, p.vs[2], true, STEP, xb);
 
   // ---- pass 2: per-head max, exponentials, sums --------------------------------
   float m[G], l[G];
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   };
   for (int base = 0; base < n_rows; base += 2 * STEP) {
     const bool second = base + STEP < n_rows;
-    if (second) load_rows(Vp, p.vs[2], true, base + STEP, xb);
+    if (second && (!V2 || base > 0)) load_rows(Vp, p.vs[2], true, base + STEP, xb);
     pv_rows(base, xa);
     if (second) {
       if (base + 2 * STEP < n_rows) load_rows(Vp, p.vs[2], true, base + 2 * STEP, xa);
