@@ -117,10 +117,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int gi = lane >> 4, si = lane & 15;
 
   const int NQ = (p.Sq + kBM - 1) / kBM;
-  const int total = NQ * p.Hq * p.B;
-  const int L = xcd_logical_id(blockIdx.x, total);
-  const int qb = NQ - 1 - L % NQ;
-  const int bh = L / NQ;
+  int bh, qb;
+  query_tile_unit(p, NQ, bh, qb);  // the forward's order, q_order included
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int hkv = hq / p.G;
   const int q0 = qb * kBM;

@@ -79,6 +79,29 @@ __device__ __forceinline__ int xcd_logical_id(int bid, int total) {
   return x * per + min(x, rem) + j;
 }
 
+// The (b * Hq + hq, query tile) unit of this workgroup.  Without a work order
+// the last query tiles start first (longest first for causal, window and prefix
+// masks) and each XCD takes a contiguous range of units, so the query tiles of
+// a head share its L2.  With the BlockMask's q_order (each row's query tiles
+// heaviest first) and B * Hq a multiple of 8, XCD x (workgroup id % 8) takes
+// heads x, x + 8, ... and its m-th workgroup runs the (m / heads-per-XCD)-th
+// heaviest tile of one of them: every XCD starts the longest units of all its
+// heads first.
+__device__ __forceinline__ void query_tile_unit(const FwdParams& p, int NQ, int& bh, int& qb) {
+  const int BH = p.Hq * p.B;
+  if (p.bm.q_order != nullptr && BH % 8 == 0) {
+    const int x = blockIdx.x & 7, m = blockIdx.x >> 3, hpx = BH >> 3;
+    const int r = m / hpx;
+    bh = x + 8 * (m - r * hpx);
+    const int mb = p.bm.Bm > 1 ? bh / p.Hq : 0, mh = p.bm.Hm > 1 ? bh % p.Hq : 0;
+    qb = min(max(p.bm.q_order[((long long)mb * p.bm.Hm + mh) * NQ + r], 0), NQ - 1);
+  } else {
+    const int L = xcd_logical_id(blockIdx.x, NQ * BH);
+    bh = L / NQ;
+    qb = NQ - 1 - L % NQ;
+  }
+}
+
 // Waits until at most N vector-memory loads of this wave are outstanding
 // (loads complete in issue order, so everything older than the N newest is done).
 template <int N>
@@ -205,23 +228,8 @@ void fwd_kernel(FwdParams p) {
 
   // ---- which (b, hq, query tile) ------------------------------------------
   const int NQ = (p.Sq + kBM - 1) / kBM;
-  const int BH = p.Hq * p.B;
   int bh, qb;
-  if (p.bm.q_order != nullptr && BH % 8 == 0) {
-    // The BlockMask orders each row's query tiles heaviest first.  XCD x
-    // (workgroup id % 8) takes heads x, x + 8, ...; its m-th workgroup is the
-    // (m / heads-per-XCD)-th heaviest tile of one of them, so each XCD starts
-    // the longest units of all its heads first.
-    const int x = blockIdx.x & 7, m = blockIdx.x >> 3, hpx = BH >> 3;
-    const int r = m / hpx;
-    bh = x + 8 * (m - r * hpx);
-    const int mb = p.bm.Bm > 1 ? bh / p.Hq : 0, mh = p.bm.Hm > 1 ? bh % p.Hq : 0;
-    qb = min(max(p.bm.q_order[((long long)mb * p.bm.Hm + mh) * NQ + r], 0), NQ - 1);
-  } else {
-    const int L = xcd_logical_id(blockIdx.x, NQ * BH);
-    bh = L / NQ;
-    qb = NQ - 1 - L % NQ;  // later (heavier, for causal) query tiles first
-  }
+  query_tile_unit(p, NQ, bh, qb);
   const int hq = bh % p.Hq, b = bh / p.Hq;
   const int hkv = hq / p.G;
   const int q0 = qb * kBM;

@@ -141,7 +141,8 @@ typedef struct {
    * by their work, heaviest first: weight 3 per tile that runs the mask (the
    * kv_* tiles) plus 2 per tile of full_kv_* (with separate_full = 1), ties
    * broken by the larger query block; NQ <= 16384.  When it is present and
-   * B*Hq is a multiple of 8, the forward starts its (b, h, query tile) units
+   * B*Hq is a multiple of 8, the forward (and the backward's dQ pass, which
+   * has the same units) starts its (b, h, query tile) units
    * in that order, the heaviest tiles of every head of an XCD first (paper
    * review §4.3: a query tile's work is the length of its lists).  Without it
    * the forward starts the last query tiles first, which is longest-first for

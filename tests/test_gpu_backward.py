@@ -20,11 +20,11 @@ compare_grad = C.compare_grad
 
 
 def run_bwd(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense=False, per_head=False,
-            scale=0.0, **kw):
+            scale=0.0, order=None, **kw):
     import torch
     from block_sparse_attention_fa_amd import fa
     print(f"[case] bwd seed={seed} mask={mask} score={score} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Skv={Skv} D={D} "
-          f"sep={separate_full} dense={dense} per_head={per_head}", flush=True)
+          f"sep={separate_full} dense={dense} per_head={per_head} order={order}", flush=True)
     q, k, v = gen.qkv(seed, B, Hq, Hkv, Sq, Skv, D)
     dO = gen._normal_bf16([seed, 30], (B, Hq, Sq, D), 1.0)
     spec = C.make_spec(seed, mask, score, B, Hq, Sq, Skv, **kw)
@@ -33,7 +33,8 @@ def run_bwd(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense
     if not dense:
         Bm = B if mask in BATCH_DEP else 1
         Hm = Hq if per_head else 1
-        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True)
+        bm = fa.fa_build_block_mask(C.gpu_mask(spec), Bm, Hm, Sq, Skv, separate_full=separate_full, transposed=True,
+                                    order=order)
     sc = C.gpu_score(spec)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
     out = fa.fa_forward(qt, kt, vt, block_mask=bm, score=sc, lse=lse, scale=scale)
@@ -41,8 +42,21 @@ def run_bwd(seed, mask, score, B, Hq, Hkv, Sq, Skv, D, separate_full=True, dense
     torch.cuda.synchronize()
     refs = fo.attention_backward(q, k, v, dO, None if dense else C.oracle_mask(spec), C.oracle_score(spec, Hq),
                                  scale=scale if scale > 0 else None)
-    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
-        compare_grad(gen.bf16_bits_to_f32(gen.from_torch_bf16(g)), r, f"{name} {mask}/{score} D={D}")
+    got = [gen.bf16_bits_to_f32(gen.from_torch_bf16(g)) for g in (dq, dk, dv)]
+    for name, g, r in zip(("dQ", "dK", "dV"), got, refs):
+        compare_grad(g, r, f"{name} {mask}/{score} D={D}")
+    return got
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("mask", ["document_causal", "causal"])
+def test_backward_work_order(mask, per_head):
+    """bwd_dq follows the BlockMask's q_order like the forward (B*Hq a multiple of 8):
+    gradients match the oracle and are bit-identical to the natural order."""
+    a = run_bwd(53, mask, "alibi", 2, 8, 2, 700, 700, 64, per_head=per_head, order=True)
+    b = run_bwd(53, mask, "alibi", 2, 8, 2, 700, 700, 64, per_head=per_head, order=False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("D", [64, 128])
