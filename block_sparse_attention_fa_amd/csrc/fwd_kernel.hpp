@@ -84,15 +84,16 @@ __device__ __forceinline__ int xcd_logical_id(int bid, int total) {
 // masks) and each XCD takes a contiguous range of units, so the query tiles of
 // a head share its L2.  With the BlockMask's q_order (each row's query tiles
 // heaviest first) and B * Hq a multiple of 8, XCD x (workgroup id % 8) takes
-// heads x, x + 8, ... and its m-th workgroup runs the (m / heads-per-XCD)-th
-// heaviest tile of one of them: every XCD starts the longest units of all its
-// heads first.
+// the x-th eighth of the (b, hq) heads, a contiguous block (the query heads of
+// a GQA group, which read the same K/V, stay on one XCD), and its m-th
+// workgroup runs the (m / heads-per-XCD)-th heaviest tile of one of them:
+// every XCD starts the longest units of all its heads first.
 __device__ __forceinline__ void query_tile_unit(const FwdParams& p, int NQ, int& bh, int& qb) {
   const int BH = p.Hq * p.B;
   if (p.bm.q_order != nullptr && BH % 8 == 0) {
     const int x = blockIdx.x & 7, m = blockIdx.x >> 3, hpx = BH >> 3;
     const int r = m / hpx;
-    bh = x + 8 * (m - r * hpx);
+    bh = x * hpx + (m - r * hpx);
     const int mb = p.bm.Bm > 1 ? bh / p.Hq : 0, mh = p.bm.Hm > 1 ? bh % p.Hq : 0;
     qb = min(max(p.bm.q_order[((long long)mb * p.bm.Hm + mh) * NQ + r], 0), NQ - 1);
   } else {
