@@ -163,26 +163,36 @@ __global__ __launch_bounds__(64) void transpose_block_lists_kernel(BuildParams p
   }
 }
 
-// Work order of the query blocks (the BlockMask's optional q_order): one
-// 1024-thread workgroup per (b', h') row sorts the keys (weight << 14) | qb in
-// LDS with a bitonic network, largest first, and writes their qb.  weight =
-// 3 per listed tile that runs the mask_mod + 2 per full tile, at most 3 NK <
-// 2^16, and qb < 2^14, so the keys are distinct and fit 30 bits.  Slots past
-// NQ hold 0, which sorts after every real key except (weight 0, qb 0), whose
-// decoded qb is the same.
+// Work orders (the BlockMask's optional q_order and kv_order): one 1024-thread
+// workgroup per (b', h') row sorts the n keys (weight << 14) | i, i < n, in LDS
+// with a bitonic network, largest first, and writes their i.  weight = 3 per
+// listed tile that runs the mask_mod + 2 per full tile, at most 3 * 16384 <
+// 2^16, and i < 2^14, so the keys are distinct and fit 30 bits.  Slots past n
+// hold 0, which sorts after every real key except (weight 0, i 0), whose
+// decoded i is the same.  For the query blocks the counts are the row lists'
+// (ties to the larger query block: key i = qb); for the KV blocks the
+// transposed view's (ties to the smaller KV block: key i = n - 1 - kb).
 constexpr int kOrderMax = 16384;
 constexpr int kOrderThreads = 1024;
-__global__ __launch_bounds__(kOrderThreads) void order_query_blocks_kernel(BuildParams p) {
+struct OrderArgs {
+  const int* num;   // [rows, n] tiles that run the mask
+  const int* full;  // [rows, n] full tiles
+  int* out;         // [rows, n]
+  int n;
+  int separate_full;
+  int reverse;      // key index n - 1 - i (ties to the smaller i)
+};
+__global__ __launch_bounds__(kOrderThreads) void order_blocks_kernel(OrderArgs a, int Hm) {
   __shared__ uint32_t key[kOrderMax];
-  const long long bh = (long long)blockIdx.y * p.Hm + blockIdx.x;
+  const long long bh = (long long)blockIdx.y * Hm + blockIdx.x;
   int n = 2;
-  while (n < p.NQ) n <<= 1;
+  while (n < a.n) n <<= 1;
   for (int i = threadIdx.x; i < n; i += kOrderThreads) {
     uint32_t k = 0;
-    if (i < p.NQ) {
-      const long long row = bh * p.NQ + i;
-      const int w = 3 * p.kv_num[row] + (p.separate_full ? 2 * p.full_num[row] : 0);
-      k = ((uint32_t)w << 14) | (uint32_t)i;
+    if (i < a.n) {
+      const long long at = bh * a.n + i;
+      const int w = 3 * a.num[at] + (a.separate_full ? 2 * a.full[at] : 0);
+      k = ((uint32_t)w << 14) | (uint32_t)(a.reverse ? a.n - 1 - i : i);
     }
     key[i] = k;
   }
@@ -192,18 +202,21 @@ __global__ __launch_bounds__(kOrderThreads) void order_query_blocks_kernel(Build
       for (int i = threadIdx.x; i < n; i += kOrderThreads) {
         const int l = i ^ j;
         if (l > i) {
-          const uint32_t a = key[i], b = key[l];
+          const uint32_t x = key[i], y = key[l];
           const bool desc = (i & k) == 0;  // this pair's subsequence runs largest first
-          if (desc ? a < b : a > b) {
-            key[i] = b;
-            key[l] = a;
+          if (desc ? x < y : x > y) {
+            key[i] = y;
+            key[l] = x;
           }
         }
       }
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < p.NQ; i += kOrderThreads) p.q_order[bh * p.NQ + i] = (int)(key[i] & 0x3fffu);
+  for (int i = threadIdx.x; i < a.n; i += kOrderThreads) {
+    const int d = (int)(key[i] & 0x3fffu);
+    a.out[bh * a.n + i] = a.reverse ? a.n - 1 - d : d;
+  }
 }
 
 struct LaunchBuild {
@@ -216,7 +229,11 @@ struct LaunchBuild {
     if (p.q_num != nullptr)
       hipLaunchKernelGGL(transpose_block_lists_kernel, dim3(p.NK, p.Hm, p.Bm), dim3(64), 0, stream, p);
     if (p.q_order != nullptr)
-      hipLaunchKernelGGL(order_query_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream, p);
+      hipLaunchKernelGGL(order_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream,
+                         OrderArgs{p.kv_num, p.full_num, p.q_order, p.NQ, p.separate_full, 0}, p.Hm);
+    if (p.kv_order != nullptr)  // after the transposed view, which it reads
+      hipLaunchKernelGGL(order_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream,
+                         OrderArgs{p.q_num, p.full_q_num, p.kv_order, p.NK, p.separate_full, 1}, p.Hm);
   }
 };
 

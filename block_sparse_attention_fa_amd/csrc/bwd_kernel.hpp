@@ -369,10 +369,24 @@ void bwd_dkdv_kernel(BwdParams P) {
   const int gi = lane >> 4, si = lane & 15;
 
   const int NK = (p.Skv + kBN - 1) / kBN;
-  const int total = NK * p.Hkv * p.B;
-  const int L = xcd_logical_id(blockIdx.x, total);
-  const int kb = L % NK;
-  const int bh = L / NK;
+  const int BHk = p.Hkv * p.B;
+  int bh, kb;
+  if (P.kv_order != nullptr && p.bm.Hm == 1 && BHk % 8 == 0) {
+    // The BlockMask orders each column's KV blocks heaviest first (one order for
+    // every head, Hm = 1).  XCD x (workgroup id % 8) takes the x-th eighth of
+    // the (b, hkv) heads, a contiguous block, and its m-th workgroup runs the
+    // (m / heads-per-XCD)-th heaviest KV block of one of them.
+    const int x = blockIdx.x & 7, m = blockIdx.x >> 3, hpx = BHk >> 3;
+    const int r = m / hpx;
+    bh = x * hpx + (m - r * hpx);
+    const int mb = p.bm.Bm > 1 ? bh / p.Hkv : 0;
+    kb = min(max(P.kv_order[(long long)mb * NK + r], 0), NK - 1);
+  } else {
+    // first KV blocks first: longest first for causal masks
+    const int L = xcd_logical_id(blockIdx.x, NK * BHk);
+    kb = L % NK;
+    bh = L / NK;
+  }
   const int hkv = bh % p.Hkv, b = bh / p.Hkv;
   const int k0 = kb * kBN;
 

@@ -269,6 +269,7 @@ fa_status prepare_backward(const fa_attn_args* a, const fa_grad_args* g, BwdPara
   P.q_num = bm ? bm->q_num_blocks : nullptr;
   P.q_idx = bm ? bm->q_indices : nullptr;
   P.full_q_num = bm ? bm->full_q_num_blocks : nullptr;
+  P.kv_order = bm ? bm->kv_order : nullptr;
   P.full_q_idx = bm ? bm->full_q_indices : nullptr;
   return FA_OK;
 }
@@ -372,6 +373,10 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
                              "full_q_num_blocks and full_q_indices (or none)");
   if (bm->q_order != nullptr && bm->NQ > 16384)
     return fail(FA_ERR_UNSUPPORTED, "q_order needs NQ <= 16384 (got %d)", bm->NQ);
+  if (bm->kv_order != nullptr && n_transposed != 4)
+    return fail(FA_ERR_NULL, "kv_order is built from the transposed view, which is not requested");
+  if (bm->kv_order != nullptr && bm->NK > 16384)
+    return fail(FA_ERR_UNSUPPORTED, "kv_order needs NK <= 16384 (got %d)", bm->NK);
   fa_status st = check_mask(bm->mask, Sq, Skv);
   if (st != FA_OK) return st;
 
@@ -385,6 +390,7 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   p.full_q_num = bm->full_q_num_blocks;
   p.full_q_idx = bm->full_q_indices;
   p.q_order = bm->q_order;
+  p.kv_order = bm->kv_order;
   p.Bm = bm->Bm;
   p.Hm = bm->Hm;
   p.NQ = bm->NQ;

@@ -82,6 +82,7 @@ struct BwdParams {
   const int* q_idx;
   const int* full_q_num;
   const int* full_q_idx;
+  const int* kv_order;    // nullptr, or each column's KV blocks heaviest first [Bm,Hm,NK]
   float* ws_lse2;         // [B, Hq, sq_pad] base-2 LSE, +inf for rows without keys
   float* ws_delta;        // [B, Hq, sq_pad] rowsum(dO * O)
   int sq_pad;             // Sq rounded up to whole 128-row tiles
@@ -97,6 +98,7 @@ struct BuildParams {
   int* full_q_num;
   int* full_q_idx;
   int* q_order;     // work order of the query blocks, nullptr when not requested
+  int* kv_order;    // work order of the KV blocks (from the transposed view), nullptr when not requested
   int Bm, Hm, NQ, NK, Sq, Skv;
   int separate_full;
   MaskParams mask;

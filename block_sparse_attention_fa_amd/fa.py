@@ -24,8 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 # --- enums (include/fa.h) ----------------------------------------------------
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 FA_BLOCK = 128
-ABI_VERSION = 4          # the layout of the structs below (include/fa.h FA_ABI_VERSION)
-MAX_ORDER_NQ = 16384     # largest NQ for which fa_build_block_mask can write q_order
+ABI_VERSION = 5          # the layout of the structs below (include/fa.h FA_ABI_VERSION)
+MAX_ORDER_NQ = 16384     # largest NQ (NK) for which fa_build_block_mask can write q_order (kv_order)
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_SLIDING_CAUSAL = 0, 1, 2, 3
 MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL, MASK_PREFIX_LM, MASK_KV_LEN = 4, 5, 6, 7
@@ -56,7 +56,7 @@ class BlockMaskC(ctypes.Structure):
                 ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc),
                 ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
                 ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p),
-                ("q_order", c_void_p)]
+                ("q_order", c_void_p), ("kv_order", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -293,6 +293,11 @@ class BlockMask:
         if order and NQ <= MAX_ORDER_NQ:
             self.q_order = torch.empty((Bm, Hm, NQ), **z)
             c.q_order = self.q_order.data_ptr()
+        # the same for the KV blocks (the backward's dK/dV pass), from the transposed view
+        self.kv_order = None
+        if order and self.transposed and NK <= MAX_ORDER_NQ:
+            self.kv_order = torch.empty((Bm, Hm, NK), **z)
+            c.kv_order = self.kv_order.data_ptr()
 
     def list_every_tile(self):
         """Re-encode as "no block skipping": every tile of every row is listed as
@@ -357,8 +362,9 @@ def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, devi
                         transposed=False, order=None):
     """Allocate a BlockMask and build it on the device (asynchronously on `stream`);
     transposed=True also builds the per-KV-block view the backward needs, and
-    order=True the heaviest-first work order of the query blocks (q_order;
-    None: for document masks only)."""
+    order=True the heaviest-first work orders of the query blocks (q_order)
+    and, with the transposed view, of the KV blocks (kv_order); None: for
+    document masks only."""
     mask.check(Bm, Sq, Skv)
     with _on(stream):
         bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed, order)

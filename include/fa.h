@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 #define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
 
 typedef enum {
@@ -152,6 +152,17 @@ typedef struct {
    * others do not (one more dependent load per workgroup).  The order changes
    * no result, only which workgroups run together. */
   int32_t* q_order;
+  /* Work order of the KV blocks (optional; NULL = none): [Bm,Hm,NK] device int32
+   * that fa_build_block_mask fills from the transposed view (which must then be
+   * requested too) with each column's KV blocks sorted by their work, heaviest
+   * first: 3 per entry of q_* and 2 per entry of full_q_* (with separate_full =
+   * 1), ties broken by the smaller KV block; NK <= 16384.  The backward's dK/dV
+   * pass, whose units are (b, hkv, KV block), starts them in that order when
+   * Hm = 1 and B*Hkv is a multiple of 8, the heaviest blocks of every head of
+   * an XCD first.  Like q_order it changes no result, and it pays off for
+   * document masks (the natural order, first KV blocks first, is already
+   * longest-first for causal masks). */
+  int32_t* kv_order;
 } fa_block_mask;
 
 /* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 4
+    assert L.fa_abi_version() == 5
     for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                                  "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
         assert L.fa_status_string(code).decode() == name
@@ -227,6 +227,20 @@ def test_q_order_needs_nq_at_most_16384():
     c = _bm(NQ=16385, NK=1, kind=fa.MASK_NONE, Sq=S, Skv=128)
     c.q_order = 0x30000
     assert fa.lib().fa_build_block_mask(ctypes.byref(c), S, 128, None) == fa.FA_ERR_UNSUPPORTED
+    assert b"16384" in fa.lib().fa_last_error()
+
+
+def test_kv_order_needs_the_transposed_view_and_nk_at_most_16384():
+    """kv_order is sorted from the transposed view's counts: refused without that
+    view, and past 16384 KV blocks (before any launch)."""
+    c = _bm()
+    c.kv_order = 0x30000
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), 256, 256, None) == fa.FA_ERR_NULL
+    S = 128 * 16385
+    c = _bm(NQ=1, NK=16385, kind=fa.MASK_NONE, Sq=128, Skv=S)
+    c.q_num_blocks = c.q_indices = c.full_q_num_blocks = c.full_q_indices = 0x20000
+    c.kv_order = 0x30000
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), 128, S, None) == fa.FA_ERR_UNSUPPORTED
     assert b"16384" in fa.lib().fa_last_error()
 
 

@@ -29,7 +29,22 @@ def _check_bitexact(spec, Bm, Hm, Sq, Skv, separate_full=True):
     assert bm.q_order is not None
     np.testing.assert_array_equal(bm.q_order.cpu().numpy(), expected_q_order(ref, separate_full),
                                   err_msg=f"{spec['mask']} q_order Sq={Sq} Skv={Skv}")
+    assert bm.kv_order is not None
+    np.testing.assert_array_equal(bm.kv_order.cpu().numpy(), expected_kv_order(ref, separate_full),
+                                  err_msg=f"{spec['mask']} kv_order Sq={Sq} Skv={Skv}")
     return bm, ref
+
+
+def expected_kv_order(ref, separate_full):
+    """The KV-block work order (include/fa.h, kv_order): each column's KV blocks by
+    weight 3 per tile of q_* + 2 per tile of full_q_*, heaviest first, ties by
+    the smaller KV block; computed from the oracle's transposed counts."""
+    w = 3 * ref["q_num_blocks"].astype(np.int64) + (2 * ref["full_q_num_blocks"].astype(np.int64) if separate_full else 0)
+    out = np.empty(w.shape, dtype=np.int32)
+    kb = np.arange(w.shape[-1])
+    for idx in np.ndindex(*w.shape[:-1]):
+        out[idx] = np.lexsort((kb, -w[idx]))
+    return out
 
 
 def expected_q_order(ref, separate_full):
