@@ -231,6 +231,9 @@ struct LaunchBuild {
     if (p.q_order != nullptr)
       hipLaunchKernelGGL(order_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream,
                          OrderArgs{p.kv_num, p.full_num, p.q_order, p.NQ, p.separate_full, 0}, p.Hm);
+    if (p.row_order != nullptr)  // one query block and one head row: the rows' counts are contiguous
+      hipLaunchKernelGGL(order_blocks_kernel, dim3(1, 1), dim3(kOrderThreads), 0, stream,
+                         OrderArgs{p.kv_num, p.full_num, p.row_order, p.Bm, p.separate_full, 1}, 1);
     if (p.kv_order != nullptr)  // after the transposed view, which it reads
       hipLaunchKernelGGL(order_blocks_kernel, dim3(p.Hm, p.Bm), dim3(kOrderThreads), 0, stream,
                          OrderArgs{p.q_num, p.full_q_num, p.kv_order, p.NK, p.separate_full, 1}, p.Hm);

@@ -74,7 +74,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
   constexpr int RPW = 64 / LPR;       // rows per wave per load
   constexpr int RSTEP = kDecWaves * RPW;
   const FwdParams& p = P.f;
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  // with the BlockMask's row order, the grid's sequences run longest first
+  const int split = blockIdx.x, hkv = blockIdx.y;
+  const int b = P.row_order != nullptr ? min(max(P.row_order[blockIdx.z], 0), (int)gridDim.z - 1) : (int)blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPR, rr = lane / LPR;
 

@@ -287,6 +287,9 @@ fa_status run_decode(const fa_attn_args* a, const FwdParams& p, int mask_kind, c
   P.pt_stride = a->page_table_stride;
   P.num_pages = a->num_pages;
   P.q_pos = a->q_pos;
+  const fa_block_mask* bm = a->block_mask;
+  P.row_order = (bm != nullptr && bm->row_order != nullptr && bm->Bm == a->B && bm->NQ == 1 && bm->Hm == 1)
+                    ? bm->row_order : nullptr;
   const fa_status st = launch_decode(a->D, a->Hq / a->Hkv, a->score.kind, P, stream);
   if (st != FA_OK) return fail(st, "decode launch failed");
   return FA_OK;
@@ -377,6 +380,10 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
     return fail(FA_ERR_NULL, "kv_order is built from the transposed view, which is not requested");
   if (bm->kv_order != nullptr && bm->NK > 16384)
     return fail(FA_ERR_UNSUPPORTED, "kv_order needs NK <= 16384 (got %d)", bm->NK);
+  if (bm->row_order != nullptr && (bm->NQ != 1 || bm->Hm != 1))
+    return fail(FA_ERR_SHAPE, "row_order needs one query block and one head row (NQ = %d, Hm = %d)", bm->NQ, bm->Hm);
+  if (bm->row_order != nullptr && bm->Bm > 16384)
+    return fail(FA_ERR_UNSUPPORTED, "row_order needs Bm <= 16384 (got %d)", bm->Bm);
   fa_status st = check_mask(bm->mask, Sq, Skv);
   if (st != FA_OK) return st;
 
@@ -391,6 +398,7 @@ fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* 
   p.full_q_idx = bm->full_q_indices;
   p.q_order = bm->q_order;
   p.kv_order = bm->kv_order;
+  p.row_order = bm->row_order;
   p.Bm = bm->Bm;
   p.Hm = bm->Hm;
   p.NQ = bm->NQ;

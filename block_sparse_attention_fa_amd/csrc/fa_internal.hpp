@@ -68,6 +68,7 @@ struct DecodeParams {
   long long pt_stride;    // page-table entries between sequences
   int num_pages;
   const int* q_pos;       // nullptr: query position 0; else position of sequence b's query
+  const int* row_order;   // nullptr, or the sequences longest first [B] (grid z -> b)
 };
 
 struct BwdParams {
@@ -99,6 +100,7 @@ struct BuildParams {
   int* full_q_idx;
   int* q_order;     // work order of the query blocks, nullptr when not requested
   int* kv_order;    // work order of the KV blocks (from the transposed view), nullptr when not requested
+  int* row_order;   // work order of the batch rows (NQ = Hm = 1), nullptr when not requested
   int Bm, Hm, NQ, NK, Sq, Skv;
   int separate_full;
   MaskParams mask;

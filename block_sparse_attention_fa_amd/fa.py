@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 # --- enums (include/fa.h) ----------------------------------------------------
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(6)
 FA_BLOCK = 128
-ABI_VERSION = 5          # the layout of the structs below (include/fa.h FA_ABI_VERSION)
+ABI_VERSION = 6          # the layout of the structs below (include/fa.h FA_ABI_VERSION)
 MAX_ORDER_NQ = 16384     # largest NQ (NK) for which fa_build_block_mask can write q_order (kv_order)
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_SLIDING_CAUSAL = 0, 1, 2, 3
@@ -56,7 +56,7 @@ class BlockMaskC(ctypes.Structure):
                 ("Sq", c_int32), ("Skv", c_int32), ("mask", MaskDesc),
                 ("q_num_blocks", c_void_p), ("q_indices", c_void_p),
                 ("full_q_num_blocks", c_void_p), ("full_q_indices", c_void_p),
-                ("q_order", c_void_p), ("kv_order", c_void_p)]
+                ("q_order", c_void_p), ("kv_order", c_void_p), ("row_order", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -287,8 +287,10 @@ class BlockMask:
         # masks, whose work per query tile follows the position inside the
         # document; the causal, window and prefix masks already have the
         # heaviest tiles last, which the forward starts first without it.
+        # Decode masks (one query block, several batch rows) get the order of
+        # their rows instead: fa_decode starts the longest sequences first.
         if order is None:
-            order = mask.kind in (MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL)
+            order = mask.kind in (MASK_DOCUMENT, MASK_DOCUMENT_CAUSAL) or (NQ == 1 and Hm == 1 and Bm > 1)
         self.q_order = None
         if order and NQ <= MAX_ORDER_NQ:
             self.q_order = torch.empty((Bm, Hm, NQ), **z)
@@ -298,6 +300,10 @@ class BlockMask:
         if order and self.transposed and NK <= MAX_ORDER_NQ:
             self.kv_order = torch.empty((Bm, Hm, NK), **z)
             c.kv_order = self.kv_order.data_ptr()
+        self.row_order = None
+        if order and NQ == 1 and Hm == 1 and 1 < Bm <= MAX_ORDER_NQ:
+            self.row_order = torch.empty((Bm,), **z)
+            c.row_order = self.row_order.data_ptr()
 
     def list_every_tile(self):
         """Re-encode as "no block skipping": every tile of every row is listed as
@@ -363,8 +369,9 @@ def fa_build_block_mask(mask: MaskMod, Bm, Hm, Sq, Skv, separate_full=True, devi
     """Allocate a BlockMask and build it on the device (asynchronously on `stream`);
     transposed=True also builds the per-KV-block view the backward needs, and
     order=True the heaviest-first work orders of the query blocks (q_order)
-    and, with the transposed view, of the KV blocks (kv_order); None: for
-    document masks only."""
+    and, with the transposed view, of the KV blocks (kv_order), and for masks of
+    one query block the order of the batch rows (row_order); None: for document
+    masks and for masks of one query block over several rows (decode)."""
     mask.check(Bm, Sq, Skv)
     with _on(stream):
         bm = BlockMask(mask, Bm, Hm, Sq, Skv, separate_full, device, transposed, order)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 #define FA_BLOCK 128 /* the only supported BLOCK_SIZE (Concepts, "BlockMask Internals": default 128x128) */
 
 typedef enum {
@@ -163,6 +163,16 @@ typedef struct {
    * document masks (the natural order, first KV blocks first, is already
    * longest-first for causal masks). */
   int32_t* kv_order;
+  /* Work order of the batch rows (optional; NULL = none), for BlockMasks of one
+   * query block and one head row (NQ = 1, Hm = 1: the decode masks): [Bm]
+   * device int32 that fa_build_block_mask fills with the rows sorted by their
+   * listed tiles, heaviest first (3 per kv_* tile, 2 per full_kv_* tile with
+   * separate_full = 1), ties to the smaller row; Bm <= 16384.  fa_decode with
+   * Bm = B starts the longest sequences' workgroups first, so that the short
+   * ones, not the long ones, run at the end of the launch (the talk summary's
+   * Flex Decoding: the key axis of each sequence split into chunks).  Changes
+   * no result.  Errors: FA_ERR_SHAPE for NQ > 1 or Hm > 1. */
+  int32_t* row_order;
 } fa_block_mask;
 
 /* Attention call arguments.  Q/O are [B,Hq,Sq,D], K/V are [B,Hkv,Skv,D]

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = fa.lib()
-    assert L.fa_abi_version() == 5
+    assert L.fa_abi_version() == 6
     for code, name in enumerate(["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
                                  "FA_ERR_WORKSPACE", "FA_ERR_HIP"]):
         assert L.fa_status_string(code).decode() == name
@@ -242,6 +242,17 @@ def test_kv_order_needs_the_transposed_view_and_nk_at_most_16384():
     c.kv_order = 0x30000
     assert fa.lib().fa_build_block_mask(ctypes.byref(c), 128, S, None) == fa.FA_ERR_UNSUPPORTED
     assert b"16384" in fa.lib().fa_last_error()
+
+
+def test_row_order_needs_one_query_block_and_head_row():
+    """row_order sorts batch rows of a one-query-block mask (decode): refused for
+    NQ > 1 or Hm > 1 (before any launch)."""
+    c = _bm(Bm=2, NQ=2, NK=2, kind=fa.MASK_NONE)
+    c.row_order = 0x30000
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), 256, 256, None) == fa.FA_ERR_SHAPE
+    c = _bm(Bm=2, Hm=2, NQ=1, NK=2, kind=fa.MASK_NONE, Sq=1)
+    c.row_order = 0x30000
+    assert fa.lib().fa_build_block_mask(ctypes.byref(c), 1, 256, None) == fa.FA_ERR_SHAPE
 
 
 def _rt_swizzle(D, r):

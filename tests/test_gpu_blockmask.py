@@ -32,6 +32,11 @@ def _check_bitexact(spec, Bm, Hm, Sq, Skv, separate_full=True):
     assert bm.kv_order is not None
     np.testing.assert_array_equal(bm.kv_order.cpu().numpy(), expected_kv_order(ref, separate_full),
                                   err_msg=f"{spec['mask']} kv_order Sq={Sq} Skv={Skv}")
+    if bm.row_order is not None:  # one query block, several rows (decode masks)
+        w = 3 * ref["kv_num_blocks"].reshape(-1).astype(np.int64) + \
+            (2 * ref["full_kv_num_blocks"].reshape(-1).astype(np.int64) if separate_full else 0)
+        np.testing.assert_array_equal(bm.row_order.cpu().numpy(), np.lexsort((np.arange(w.size), -w)),
+                                      err_msg=f"{spec['mask']} row_order")
     return bm, ref
 
 

@@ -10,11 +10,11 @@ from tests import _cases as C
 pytestmark = pytest.mark.gpu
 
 
-def _decode(q, k, v, lens, score, num_splits=0, Bm=None, extra=None):
+def _decode(q, k, v, lens, score, num_splits=0, Bm=None, extra=None, order=None):
     import torch
     from block_sparse_attention_fa_amd import fa
     B, KV = k.shape[0], k.shape[2]
-    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV)
+    bm = fa.fa_build_block_mask(fa.MaskMod("kv_len", kv_len=torch.from_numpy(lens).cuda()), B, 1, 1, KV, order=order)
     lse = torch.empty((B, q.shape[1], 1), dtype=torch.float32, device="cuda")
     out = fa.fa_decode(gen.to_torch_bf16(q), gen.to_torch_bf16(k), gen.to_torch_bf16(v), block_mask=bm,
                        score=score, num_splits=num_splits, lse=lse)
@@ -39,6 +39,23 @@ def test_decode_matches_oracle(G, D, score):
     O, L = fo.decode(q, k, v, lens, C.oracle_score(spec, Hq))
     C.compare(got, O, f"decode G={G} D={D} {score}")
     C.compare_lse(lse[..., 0], L[..., 0], "decode")
+
+
+def test_decode_row_order():
+    """With the BlockMask's row order fa_decode starts the longest sequences first;
+    output and LSE are bit-identical to the grid's own order, and match the oracle."""
+    from block_sparse_attention_fa_amd import fa
+    B, Hq, Hkv, KV, D = 6, 8, 2, 3000, 128
+    q = gen.qkv(60, B, Hq, Hkv, 1, KV, D)[0]
+    _, k, v = gen.qkv(61, B, Hkv, Hkv, 1, KV, D)
+    lens = np.array([129, 3000, 1, 2048, 700, 2999], dtype=np.int32)
+    sc = fa.ScoreMod("softcap", softcap=50.0)
+    a, la = _decode(q, k, v, lens, sc, order=True)
+    b, lb = _decode(q, k, v, lens, sc, order=False)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    O, L = fo.decode(q, k, v, lens, fo.softcap(50.0))
+    C.compare(a, O, "decode with row order")
+    C.compare_lse(la[..., 0], L[..., 0], "decode with row order")
 
 
 def test_split_count_invariance_and_forward_equivalence():
