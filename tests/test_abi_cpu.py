@@ -409,3 +409,35 @@ def test_noalloc_decode_size_limit_is_checked_on_the_host():
     assert "scratch" in fa.lib().fa_last_error().decode()
     a = _args(Sq=2)
     assert fa.lib().fa_decode_noalloc(ctypes.byref(a), None) == fa.FA_ERR_SHAPE
+
+
+def test_binding_structs_match_the_c_layout(tmp_path):
+    """Every ctypes struct of the binding has the size and field offsets the C
+    compiler gives the matching struct of include/fa.h (a mismatch would pass
+    wrong values through the ABI without any error)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    pairs = [("fa_mask_desc", fa.MaskDesc), ("fa_score_desc", fa.ScoreDesc), ("fa_block_mask", fa.BlockMaskC),
+             ("fa_attn_args", fa.AttnArgs), ("fa_grad_args", fa.GradArgs)]
+    lines = ['#include <stdio.h>', '#include "fa.h"', "int main(void) {"]
+    for cname, py in pairs:
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        c, f, v = line.split()
+        got[(c, f)] = int(v)
+    for cname, py in pairs:
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, f"{cname}.{fname}"
