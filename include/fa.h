@@ -247,10 +247,13 @@ fa_status fa_block_mask_dims(int32_t Sq, int32_t Skv, int32_t block_q, int32_t b
  * descriptor filled in; on success bm->Sq and bm->Skv are set.  Every entry
  * of the four tensors is written (padding included).  The mask is evaluated
  * for b' < Bm and h' < Hm.
- * Errors: FA_ERR_NULL (tensor pointers, doc_ids/kv_len needed by the kind),
- * FA_ERR_SHAPE (NQ/NK not matching Sq/Skv, Bm or Hm < 1, Sq != Skv for a
- * document kind, negative window/prefix), FA_ERR_UNSUPPORTED (block size,
- * unknown kind), FA_ERR_HIP. */
+ * The optional work orders (q_order, kv_order, row_order) are written when
+ * their pointers are set.
+ * Errors: FA_ERR_NULL (tensor pointers, doc_ids/kv_len needed by the kind,
+ * kv_order without the transposed view), FA_ERR_SHAPE (NQ/NK not matching
+ * Sq/Skv, Bm or Hm < 1, Sq != Skv for a document kind, negative
+ * window/prefix, row_order with NQ > 1 or Hm > 1), FA_ERR_UNSUPPORTED (block
+ * size, unknown kind, an order longer than 16384), FA_ERR_HIP. */
 fa_status fa_build_block_mask(fa_block_mask* bm, int32_t Sq, int32_t Skv, void* stream);
 
 /* Fused block-sparse attention forward (paper review §2.1, §3.3, §4.2-4.3):
