@@ -110,3 +110,27 @@ def test_blockmask_rebuild_reuses_buffers():
         docs = gen.document_ids(seed, 1, S, 100, 700)
         spec = {"mask": "document_causal", "docs": docs}
         _check_bitexact(spec, 1, 1, S, S)
+
+
+def test_work_orders_past_one_workgroup_of_threads():
+    """The order kernel sorts more entries than its 1024 threads (NQ = NK = 2344,
+    not a power of two): q_order and kv_order equal the orders lexsort gives for
+    the built counts (the counts themselves are checked against the oracle at
+    the smaller sizes above), and each is a permutation."""
+    from block_sparse_attention_fa_amd import fa
+    import torch
+    S = 300000
+    docs = gen.document_ids(9, 1, S, 1000, 40000)
+    mask = fa.MaskMod("document_causal", doc_ids=torch.from_numpy(docs).cuda())
+    bm = fa.fa_build_block_mask(mask, 1, 1, S, S, transposed=True, order=True)
+    torch.cuda.synchronize()
+    assert bm.NQ == 2344 and bm.q_order is not None and bm.kv_order is not None
+    w = 3 * bm.kv_num_blocks.cpu().numpy().reshape(-1).astype(np.int64) + \
+        2 * bm.full_kv_num_blocks.cpu().numpy().reshape(-1).astype(np.int64)
+    qb = np.arange(bm.NQ)
+    np.testing.assert_array_equal(bm.q_order.cpu().numpy().reshape(-1), np.lexsort((-qb, -w)))
+    wk = 3 * bm.q_num_blocks.cpu().numpy().reshape(-1).astype(np.int64) + \
+        2 * bm.full_q_num_blocks.cpu().numpy().reshape(-1).astype(np.int64)
+    kb = np.arange(bm.NK)
+    np.testing.assert_array_equal(bm.kv_order.cpu().numpy().reshape(-1), np.lexsort((kb, -wk)))
+
