@@ -155,9 +155,9 @@ def test_decode_validation_and_workspace_size():
         assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
         assert n.value == splits * 2 * 8 * (128 + 1) * 4, ns
     a.num_splits = 0
-    a.B, a.Hkv, a.Hq, a.Skv = 32, 8, 32, 32768  # 256 tiles, 256 (b, kv head) pairs: 6-tile chunks
+    a.B, a.Hkv, a.Hq, a.Skv = 32, 8, 32, 32768  # 256 tiles, 256 (b, kv head) pairs: 7-tile chunks
     assert fa.lib().fa_decode_workspace_size(ctypes.byref(a), ctypes.byref(n)) == fa.FA_OK
-    assert n.value == 43 * 32 * 32 * (128 + 1) * 4
+    assert n.value == 37 * 32 * 32 * (128 + 1) * 4
     a = _args(Sq=2)
     assert _status(a, decode=True) == fa.FA_ERR_SHAPE
     a = _args(Hq=6, Hkv=2, Sq=1)
